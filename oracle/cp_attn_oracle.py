@@ -1,0 +1,419 @@
+"""fp64 CPU oracle for one context-parallel rank's share of packed causal attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module. The product path never
+does; it shares no code with this file.
+
+What is computed is the plain definition, written out slowly in float64 numpy:
+
+* Packed ("thd") layout with inter-sequence padding, the per-rank
+  sequence-length metadata and the value-based padding decision: page "[PyTorch]
+  [Attention] THD P2P context-parallel regression when padded cu_seqlens are
+  value-equal but not object-identical", sections "Describe the bug" and
+  "Expected behavior".
+* Load-balanced sharding into 2*CP chunks per sequence, rank r holding chunks r
+  and 2*CP-1-r: the divisibility rule is on page "Hybrid / Hierarchical Context
+  Parallel Skill", section "Enablement"; the chunk assignment itself is the
+  standard zig-zag reading (the pages do not spell it out).
+* Causal softmax attention forward (out, natural-log LSE) and its exact
+  gradient: not on the pages; the textbook definition.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+padding sits at the end of each sequence's padded slot; valid rows fill the
+2*CP chunks in order; LSE is natural log, laid out [heads, rows]; padding rows
+get out = 0, lse = -inf and zero gradients; query head h uses KV head
+h // (Hq / Hkv); the dK/dV "part" for shard s is the contribution of this
+rank's query rows only.
+
+Parity is pinned by the "not gpu" tests: brute force over an explicit mask of
+the whole pack, torch's fp64 CPU attention routine (out and LSE) and autograd,
+central finite differences, closed forms and the all-ranks invariants.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+class OracleError(ValueError):
+    pass
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def validate(cu, cup, cp: int, rank: int | None = None):
+    """Argument rules of the packed CP layout.
+
+    cu[0] = cup[0] = 0, both non-decreasing, 0 <= L_b <= P_b, and every padded
+    length divisible by 2*CP (page "Hybrid / Hierarchical Context Parallel
+    Skill", section "Enablement": sequence length must divide by 2*CP).
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    cup = np.asarray(cup, dtype=np.int64)
+    if cp < 1:
+        raise OracleError("cp_size must be >= 1")
+    if rank is not None and not (0 <= rank < cp):
+        raise OracleError("cp_rank out of range")
+    if cu.ndim != 1 or cup.shape != cu.shape or cu.size < 1:
+        raise OracleError("cu_seqlens and cu_seqlens_padded must be [B+1]")
+    if cu[0] != 0 or cup[0] != 0:
+        raise OracleError("cu_seqlens must start at 0")
+    L = np.diff(cu)
+    P = np.diff(cup)
+    if (L < 0).any() or (P < 0).any():
+        raise OracleError("cu_seqlens must be non-decreasing")
+    if (L > P).any():
+        raise OracleError("valid length exceeds padded length")
+    if (P % (2 * cp)).any():
+        raise OracleError("padded length not divisible by 2*cp")
+    return cu, cup
+
+
+# ---------------------------------------------------------------------------
+# sharding (where each global row goes)
+# ---------------------------------------------------------------------------
+
+def owner_map(cu, cup, cp: int):
+    """For every global row: (owning rank, local row on that rank).
+
+    Sequence b's padded slot [cup[b], cup[b+1]) is cut into 2*CP chunks of
+    c_b = P_b / (2*CP) rows. Chunk k belongs to rank k if k < CP and to rank
+    2*CP-1-k otherwise; on its rank the two chunks are stored in increasing
+    chunk order, the sequence's pair of chunks starting at local row
+    cup[b] / CP.
+    """
+    cu, cup = validate(cu, cup, cp)
+    T = int(cup[-1])
+    rank = np.empty(T, dtype=np.int64)
+    local = np.empty(T, dtype=np.int64)
+    for b in range(cup.size - 1):
+        P = int(cup[b + 1] - cup[b])
+        c = P // (2 * cp)
+        for q in range(P):
+            k = q // c
+            o = q % c
+            g = int(cup[b]) + q
+            if k < cp:
+                rank[g] = k
+                local[g] = int(cup[b]) // cp + o
+            else:
+                rank[g] = 2 * cp - 1 - k
+                local[g] = int(cup[b]) // cp + c + o
+    return rank, local
+
+
+def shard_rows(cu, cup, cp: int, s: int) -> np.ndarray:
+    """Global row index held at each local row of rank (= shard) s."""
+    rank, local = owner_map(cu, cup, cp)
+    T_local = int(cup[-1]) // cp
+    rows = np.full(T_local, -1, dtype=np.int64)
+    sel = np.nonzero(rank == s)[0]
+    rows[local[sel]] = sel
+    if (rows < 0).any():
+        raise OracleError("owner map does not cover every local row")
+    return rows
+
+
+def valid_mask(cu, cup) -> np.ndarray:
+    """True for global rows holding a real token (not a padding slot)."""
+    cu = np.asarray(cu, dtype=np.int64)
+    cup = np.asarray(cup, dtype=np.int64)
+    m = np.zeros(int(cup[-1]), dtype=bool)
+    for b in range(cu.size - 1):
+        m[cup[b]:cup[b] + (cu[b + 1] - cu[b])] = True
+    return m
+
+
+def gather_shard(x: np.ndarray, cu, cup, cp: int, s: int) -> np.ndarray:
+    """Rows of a global packed array that rank s holds, in its local order."""
+    return x[shard_rows(cu, cup, cp, s)]
+
+
+# ---------------------------------------------------------------------------
+# per-rank metadata (integers, exact)
+# ---------------------------------------------------------------------------
+
+def _chunk_valid(L: int, c: int, k: int) -> int:
+    """Valid rows in chunk k of a sequence with L valid rows and chunk size c:
+    valid tokens fill the chunks in order, so this is clamp(L - k*c, 0, c)."""
+    return max(0, min(c, L - k * c))
+
+
+def step_kind(cp: int, r: int, i: int) -> tuple[int, int]:
+    """(kind, source shard) of ring step i on rank r.
+
+    The shard arriving at step i comes from rank s = (r - i) mod CP. Local rows
+    are [chunk r | chunk 2CP-1-r] with increasing global position, so:
+    kind 0 (i == 0): own shard, plain causal mask on local rows;
+    kind 1 (s < r): all query rows see only chunk s (the first half of shard s),
+        with no mask (chunk s precedes both query chunks, chunk 2CP-1-s follows);
+    kind 2 (s > r): only the second query chunk sees all of shard s, with no mask.
+    """
+    s = (r - i) % cp
+    if i == 0:
+        return 0, s
+    return (1 if s < r else 2), s
+
+
+def rank_metadata(cu, cup, cp: int, r: int, t_alloc: int | None = None) -> dict:
+    """Per-rank sequence tables of rank r (all int64 numpy arrays).
+
+    The inter-sequence padding decision is taken from the values of the two
+    cumulative-length arrays, never from whether they are the same object
+    (page "[PyTorch][Attention] THD P2P context-parallel regression ...",
+    sections "Describe the bug" and "Expected behavior").
+    """
+    cu, cup = validate(cu, cup, cp, r)
+    B = cu.size - 1
+    L = np.diff(cu)
+    P = np.diff(cup)
+    c = P // (2 * cp)
+    T_local = int(cup[-1]) // cp
+    md = {
+        "B": B, "cp": cp, "rank": r, "t_local": T_local,
+        "pad_between_seqs": int(bool((cu != cup).any())),
+        "has_tail": int(t_alloc is not None and t_alloc > T_local),
+        "chunk": c.copy(),
+        "cu_padded_local": cup // cp,
+        "cu_padded_half": cup // (2 * cp),
+    }
+
+    def excl_cumsum(x):
+        out = np.zeros(B + 1, dtype=np.int64)
+        out[1:] = np.cumsum(x)
+        return out
+
+    first, second = {}, {}
+    for s in range(cp):
+        f = np.array([_chunk_valid(int(L[b]), int(c[b]), s) for b in range(B)], dtype=np.int64)
+        sc = np.array([_chunk_valid(int(L[b]), int(c[b]), 2 * cp - 1 - s) for b in range(B)], dtype=np.int64)
+        first[s], second[s] = f, sc
+        md[f"cu_full_{s}"] = excl_cumsum(f + sc)
+        md[f"cu_first_{s}"] = excl_cumsum(f)
+        md[f"cu_second_{s}"] = excl_cumsum(sc)
+    base = cup[:-1] // cp
+    steps = []
+    for i in range(cp):
+        kind, s = step_kind(cp, r, i)
+        q_start = base + (c if kind == 2 else 0)
+        q_len = second[r] if kind == 2 else first[r] + second[r]
+        kv_start = base.copy()
+        kv_len = first[s] if kind == 1 else first[s] + second[s]
+        steps.append({"kind": kind, "src": s, "q_start": q_start, "q_len": q_len,
+                      "kv_start": kv_start, "kv_len": kv_len})
+    md["steps"] = steps
+    return md
+
+
+# ---------------------------------------------------------------------------
+# attention (plain definition, float64)
+# ---------------------------------------------------------------------------
+
+def _attend_sequence(qh, kh, vh, doh, pos, scale, want_grad):
+    """One sequence, one query head.
+
+    qh: [n, D] queries at in-sequence positions ``pos`` (int array, length n);
+    kh, vh: [L, D] keys/values of the whole sequence; doh: [n, D] or None.
+    Query at position p sees keys j <= p.
+    Returns out [n, D], lse [n] and, if asked, (dq [n, D], dk [L, D], dv [L, D]).
+    """
+    L = kh.shape[0]
+    s = scale * (qh @ kh.T)                                   # [n, L]
+    allowed = np.arange(L)[None, :] <= pos[:, None]
+    s = np.where(allowed, s, NEG_INF)
+    m = s.max(axis=1)
+    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    p = np.exp(s - lse[:, None])                              # 0 where masked
+    out = p @ vh
+    if not want_grad:
+        return out, lse, None
+    dp = doh @ vh.T                                           # [n, L]
+    dcoef = (doh * out).sum(axis=1)                           # D_p = <dO_p, out_p>
+    ds = p * (dp - dcoef[:, None])
+    dq = scale * (ds @ kh)
+    dk = scale * (ds.T @ qh)
+    dv = p.T @ doh
+    return out, lse, (dq, dk, dv)
+
+
+def attention(q, k, v, do, cu, cup, scale, query_mask=None, want_grad=True,
+              max_elems: int = 1 << 25):
+    """Packed causal attention over global rows, float64.
+
+    q, k, v, do are float64 global packed arrays ([T, Hq, D], [T, Hkv, D],
+    [T, Hkv, D], [T, Hq, D]). Only the query rows where ``query_mask`` is True
+    (default: all valid rows) are computed; keys are every valid row of the
+    same sequence at or before the query. The gradient is that of
+    sum(do * out) over the selected query rows, so dK/dV collect only those
+    rows' contributions.
+
+    Returns out [T, Hq, D] (0 outside the selection), lse [Hq, T] (-inf
+    outside), and if ``want_grad``: dq [T, Hq, D], dk, dv [T, Hkv, D].
+    Query rows are processed in batches of at most ``max_elems`` scores; this
+    splits only the outer loop, every row's sums stay whole.
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    cup = np.asarray(cup, dtype=np.int64)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if hq % hkv:
+        raise OracleError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    vm = valid_mask(cu, cup)
+    if query_mask is None:
+        query_mask = vm
+    query_mask = query_mask & vm
+    out = np.zeros((T, hq, d))
+    lse = np.full((hq, T), NEG_INF)
+    if want_grad:
+        dq = np.zeros((T, hq, d))
+        dk = np.zeros((T, hkv, d))
+        dv = np.zeros((T, hkv, d))
+    for b in range(cu.size - 1):
+        base = int(cup[b])
+        Lb = int(cu[b + 1] - cu[b])
+        if Lb == 0:
+            continue
+        rows = np.nonzero(query_mask[base:base + Lb])[0]     # in-sequence positions
+        if rows.size == 0:
+            continue
+        step = max(1, max_elems // Lb)
+        for h in range(hq):
+            g = h // group
+            kh = k[base:base + Lb, g]
+            vh = v[base:base + Lb, g]
+            for a in range(0, rows.size, step):
+                pos = rows[a:a + step]
+                o, l, gr = _attend_sequence(q[base + pos, h], kh, vh,
+                                            do[base + pos, h] if want_grad else None,
+                                            pos, scale, want_grad)
+                out[base + pos, h] = o
+                lse[h, base + pos] = l
+                if want_grad:
+                    dq[base + pos, h] = gr[0]
+                    dk[base:base + Lb, g] += gr[1]
+                    dv[base:base + Lb, g] += gr[2]
+    if want_grad:
+        return out, lse, dq, dk, dv
+    return out, lse
+
+
+def share(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
+          want_grad: bool = True):
+    """Rank r's share: its query rows against every key, in r's local layout.
+
+    Returns a dict with out [T_local, Hq, D], lse [Hq, T_local], and if asked
+    dq [T_local, Hq, D] and dk_parts / dv_parts: a list over source shards s of
+    [T_local, Hkv, D] arrays, the contribution of r's query rows to the
+    gradient of shard s's keys and values, in shard s's local layout.
+    Inputs are bf16 bit arrays in the global packed layout.
+    """
+    cu, cup = validate(cu, cup, cp, r)
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_bits)
+    v = bf16_to_f64(v_bits)
+    do = bf16_to_f64(do_bits) if want_grad else None
+    rank_of, _ = owner_map(cu, cup, cp)
+    res = attention(q, k, v, do if want_grad else np.zeros_like(q), cu, cup, scale,
+                    query_mask=(rank_of == r), want_grad=want_grad)
+    own = shard_rows(cu, cup, cp, r)
+    outd = {"out": res[0][own], "lse": res[1][:, own]}
+    if want_grad:
+        outd["dq"] = res[2][own]
+        outd["dk_parts"] = [res[3][shard_rows(cu, cup, cp, s)] for s in range(cp)]
+        outd["dv_parts"] = [res[4][shard_rows(cu, cup, cp, s)] for s in range(cp)]
+    return outd
+
+
+def share_rows_forward(q_bits, k_bits, v_bits, cu, cup, cp: int, r: int, scale: float,
+                       local_rows, heads):
+    """out and lse of selected local rows / heads of rank r's share.
+
+    Each (row, head) is one full softmax row, computed on its own, so single
+    entries of a large share can be checked without the whole share.
+    Returns out [n_rows, n_heads, D] and lse [n_heads, n_rows].
+    """
+    cu, cup = validate(cu, cup, cp, r)
+    own = shard_rows(cu, cup, cp, r)
+    vm = valid_mask(cu, cup)
+    hq = q_bits.shape[1]
+    hkv = k_bits.shape[1]
+    group = hq // hkv
+    d = q_bits.shape[2]
+    local_rows = np.asarray(local_rows, dtype=np.int64)
+    out = np.zeros((local_rows.size, len(heads), d))
+    lse = np.full((len(heads), local_rows.size), NEG_INF)
+    seq_of = np.searchsorted(np.asarray(cup), np.arange(int(cup[-1])), side="right") - 1
+    for i, t in enumerate(local_rows):
+        g_row = int(own[t])
+        if not vm[g_row]:
+            continue
+        b = int(seq_of[g_row])
+        base = int(cup[b])
+        p = g_row - base
+        for j, h in enumerate(heads):
+            kv = h // group
+            qh = bf16_to_f64(q_bits[g_row, h])[None, :]
+            kh = bf16_to_f64(k_bits[base:base + p + 1, kv])
+            vh = bf16_to_f64(v_bits[base:base + p + 1, kv])
+            o, l, _ = _attend_sequence(qh, kh, vh, None, np.array([p]), scale, False)
+            out[i, j] = o[0]
+            lse[j, i] = l[0]
+    return out, lse
+
+
+def share_rows_dq(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
+                  local_rows, heads):
+    """dQ of selected local rows / heads of rank r's share (each row on its own:
+    dQ_p depends only on row p's softmax and D_p = <dO_p, out_p>)."""
+    cu, cup = validate(cu, cup, cp, r)
+    own = shard_rows(cu, cup, cp, r)
+    vm = valid_mask(cu, cup)
+    hq = q_bits.shape[1]
+    group = hq // k_bits.shape[1]
+    d = q_bits.shape[2]
+    local_rows = np.asarray(local_rows, dtype=np.int64)
+    dq = np.zeros((local_rows.size, len(heads), d))
+    seq_of = np.searchsorted(np.asarray(cup), np.arange(int(cup[-1])), side="right") - 1
+    for i, t in enumerate(local_rows):
+        g_row = int(own[t])
+        if not vm[g_row]:
+            continue
+        b = int(seq_of[g_row])
+        base = int(cup[b])
+        p = g_row - base
+        for j, h in enumerate(heads):
+            kv = h // group
+            qh = bf16_to_f64(q_bits[g_row, h])[None, :]
+            doh = bf16_to_f64(do_bits[g_row, h])[None, :]
+            kh = bf16_to_f64(k_bits[base:base + p + 1, kv])
+            vh = bf16_to_f64(v_bits[base:base + p + 1, kv])
+            _, _, gr = _attend_sequence(qh, kh, vh, doh, np.array([p]), scale, True)
+            dq[i, j] = gr[0][0]
+    return dq
+
+
+def flops_share(cu, cup, cp: int, r: int, hq: int, d: int) -> dict:
+    """Algorithmic work of rank r's share: causal (query, key) pairs over valid
+    rows (diagonal included) and the flop counts 4*D per pair per query head
+    (forward) and 10*D (backward)."""
+    cu, cup = validate(cu, cup, cp, r)
+    rank_of, _ = owner_map(cu, cup, cp)
+    vm = valid_mask(cu, cup)
+    pairs = 0
+    for b in range(cu.size - 1):
+        base = int(cup[b])
+        Lb = int(cu[b + 1] - cu[b])
+        pos = np.nonzero((rank_of[base:base + Lb] == r) & vm[base:base + Lb])[0]
+        pairs += int((pos + 1).sum())
+    return {"pairs": pairs, "fwd": 4 * d * hq * pairs, "bwd": 10 * d * hq * pairs,
+            "total": 14 * d * hq * pairs}
