@@ -1,0 +1,153 @@
+"""Python binding of the C ABI (argument marshalling only).
+
+Every function forwards to the entry point of the same name in libcpattn.so
+(include/cp_attn.h). PyTorch only provides device memory (``data_ptr``) and
+the current stream; all work runs in the library's HIP kernels. There is no
+fallback: if the library is missing these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib as L
+
+
+class CpAttnError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {L.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(rc: int, where: str):
+    if rc != L.OK:
+        msg = L.load().cp_attn_last_error().decode(errors="replace")
+        raise CpAttnError(rc, where, msg)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ptr_array(ts):
+    arr = (C.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t)
+    return arr
+
+
+class Meta:
+    """Owns a cp_attn_meta handle (freed on close / garbage collection)."""
+
+    def __init__(self, handle: int):
+        self._h = C.c_void_p(handle)
+        s = L.Summary()
+        _check(L.load().cp_attn_meta_summary(self._h, C.byref(s)), "cp_attn_meta_summary")
+        self.summary = s
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("metadata handle already freed")
+        return self._h
+
+    @property
+    def t_local(self) -> int:
+        return int(self.summary.t_local)
+
+    @property
+    def cp(self) -> int:
+        return int(self.summary.cp_size)
+
+    def steps(self):
+        s = self.summary
+        return [(int(s.step_kind[i]), int(s.step_src[i])) for i in range(s.cp_size)]
+
+    def export(self) -> np.ndarray:
+        return cp_attn_meta_export(self)
+
+    def close(self):
+        if self._h:
+            L.load().cp_attn_meta_free(self._h)
+            self._h = C.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def cp_attn_rank_metadata(cu_seqlens, cu_seqlens_padded, cp_size: int, cp_rank: int, pad_hint: int = -1,
+                          t_alloc: int | None = None, stream=None, B: int | None = None) -> Meta:
+    """cu_seqlens / cu_seqlens_padded: device int32 tensors [B+1] (padded may be
+    the same tensor, a distinct copy, or None)."""
+    if B is None:
+        B = cu_seqlens.numel() - 1
+    if t_alloc is None:
+        raise ValueError("t_alloc is required")
+    h = C.c_void_p()
+    rc = L.load().cp_attn_rank_metadata(_ptr(cu_seqlens), _ptr(cu_seqlens_padded), int(B), int(cp_size),
+                                        int(cp_rank), int(pad_hint), int(t_alloc), _stream(stream), C.byref(h))
+    _check(rc, "cp_attn_rank_metadata")
+    return Meta(h.value)
+
+
+def cp_attn_meta_export(meta: Meta) -> np.ndarray:
+    lib = L.load()
+    n = C.c_size_t()
+    _check(lib.cp_attn_meta_export(meta.handle, None, 0, C.byref(n)), "cp_attn_meta_export")
+    buf = (C.c_int32 * n.value)()
+    _check(lib.cp_attn_meta_export(meta.handle, buf, n.value, C.byref(n)), "cp_attn_meta_export")
+    return np.frombuffer(buf, dtype=np.int32).copy()
+
+
+def cp_attn_workspace_bytes(meta: Meta, hq: int, hkv: int, d: int, pass_: int) -> int:
+    return int(L.load().cp_attn_workspace_bytes(meta.handle, hq, hkv, d, pass_))
+
+
+def cp_attn_fwd(meta: Meta, q, k_shards, v_shards, hq: int, hkv: int, d: int, softmax_scale: float,
+                causal: int, out, lse, workspace, stream=None):
+    ks = _ptr_array(k_shards)
+    vs = _ptr_array(v_shards)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = L.load().cp_attn_fwd(meta.handle, _ptr(q), ks, vs, hq, hkv, d, float(softmax_scale), int(causal),
+                              _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "cp_attn_fwd")
+
+
+def cp_attn_bwd(meta: Meta, q, k_shards, v_shards, out, lse, dout, hq: int, hkv: int, d: int,
+                softmax_scale: float, causal: int, dq, dk_parts, dv_parts, workspace, stream=None):
+    ks = _ptr_array(k_shards)
+    vs = _ptr_array(v_shards)
+    dks = _ptr_array(dk_parts)
+    dvs = _ptr_array(dv_parts)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = L.load().cp_attn_bwd(meta.handle, _ptr(q), ks, vs, _ptr(out), _ptr(lse), _ptr(dout), hq, hkv, d,
+                              float(softmax_scale), int(causal), _ptr(dq), dks, dvs, _ptr(workspace), ws_bytes,
+                              _stream(stream))
+    _check(rc, "cp_attn_bwd")
+
+
+def cp_attn_shard_gather(meta: Meta, shard: int, global_rows, local_rows, row_bytes: int, stream=None):
+    rc = L.load().cp_attn_shard_gather(meta.handle, int(shard), _ptr(global_rows), _ptr(local_rows),
+                                       int(row_bytes), _stream(stream))
+    _check(rc, "cp_attn_shard_gather")
+
+
+def cp_attn_last_error() -> str:
+    return L.load().cp_attn_last_error().decode(errors="replace")

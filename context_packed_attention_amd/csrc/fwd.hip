@@ -1,0 +1,406 @@
+// Forward of one CP rank's share: one flash-style MFMA kernel per ring step,
+// then a log-sum-exp merge of the step partials.
+//
+// "thd format is not supported with hierarchical CP implementation yet": the
+// P2P ring delivers one KV shard per step and long sequences keep the ring's
+// exchange under compute. What each step computes follows from the
+// load-balanced pairing of chunks r and 2*CP-1-r ("Hybrid / Hierarchical
+// Context Parallel Skill", "Enablement"): step 0 is causal on local rows;
+// a shard from an earlier rank is seen in full by all query rows but only
+// through its first chunk; a shard from a later rank is seen in full by the
+// second query chunk only. The merge is the exact softmax identity
+//   lse = log(e^la + e^lb),  O = e^(la-lse) Oa + e^(lb-lse) Ob.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "internal.h"
+#include "kern_common.h"
+
+namespace cpattn {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* q_start;
+  const int32_t* q_len;
+  const int32_t* kv_start;
+  const int32_t* kv_len;
+  const int32_t* items;  // (sequence, tile) pairs
+  int hq, group;
+  long long ld_q, ld_kv;  // elements per row
+  float scale, c_log2;    // softmax scale, scale * log2(e)
+  int causal;
+  float* o;               // fp32 [rows, hq, D]
+  float* lse;             // fp32 [hq, ld_lse]
+  long long ld_o, ld_lse;
+};
+
+// One block = 4 wavefronts = 128 query rows of one head; each wavefront owns
+// 32 query rows. Key/value tiles of 64 rows are staged in LDS (K row-major,
+// V transposed) with a register-prefetched double buffer. Scores are computed
+// transposed (S^T = K Q^T) so each lane owns one query row: the online
+// softmax needs one cross-lane max per tile, and the output O^T = V^T P^T
+// keeps per-lane row scaling. Rescaling is lazy: the running max only moves
+// when a tile's max exceeds it by more than 2^8 in exp2 units.
+template <int D>
+__global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
+  constexpr int BM = FWD_BM, BN = 64;
+  constexpr int KS = D + 8;   // K tile row stride (bf16)
+  constexpr int VS = BN + 4;  // V^T tile row stride (bf16)
+  constexpr int NKK = D / 16;
+  constexpr int NMD = D / 32;
+  constexpr int KCH = BN * D / 8 / 256;      // 16-byte K chunks per thread
+  constexpr int VBLK = (BN / 4) * (D / 8);   // 4x8 V blocks per tile
+  static_assert(BM == 128, "4 wavefronts x 32 rows");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  int item, head;
+  map_block(blockIdx.x, p.hq, item, head);
+  const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
+  const int qs = p.q_start[sb], ql = p.q_len[sb], kvs = p.kv_start[sb], kl = p.kv_len[sb];
+  const int q0 = tile * BM;
+  const int nq = min(BM, ql - q0);
+  const int kvh = head / p.group;
+  const int n_keys = p.causal ? min(kl, q0 + nq) : kl;
+  const int nt = (n_keys + BN - 1) / BN;
+  const float c = p.c_log2;
+
+  const int qrow = q0 + w * 32 + l32;  // relative to the step's query range
+  bf16x8_t qf[NKK];
+  {
+    const bool ok = qrow < ql;
+    const uint16_t* src = p.q + (long long)(qs + (ok ? qrow : 0)) * p.ld_q + head * D + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 u = ok ? *reinterpret_cast<const uint4*>(src + kk * 16) : make_uint4(0, 0, 0, 0);
+      qf[kk] = as_bf16x8(u);
+    }
+  }
+
+  f32x16_t o[NMD];
+#pragma unroll
+  for (int md = 0; md < NMD; ++md) o[md] = zero16();
+  float m_run = NEG_INF_F, l_run = 0.f;
+
+  const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
+  const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
+  uint4 kreg[KCH];
+  uint4 vreg[4];
+  const int vkg = tid / (D / 8), vdc = tid % (D / 8);
+
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int ch = 0; ch < KCH; ++ch) {
+      const int id = tid + 256 * ch;
+      const int row = id / (D / 8), col = id % (D / 8);
+      const int key = kt * BN + row;
+      kreg[ch] = key < kl ? *reinterpret_cast<const uint4*>(kbase + (long long)key * p.ld_kv + col * 8)
+                          : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < VBLK) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt * BN + 4 * vkg + r;
+        vreg[r] = key < kl ? *reinterpret_cast<const uint4*>(vbase + (long long)key * p.ld_kv + vdc * 8)
+                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int ch = 0; ch < KCH; ++ch) {
+      const int id = tid + 256 * ch;
+      const int row = id / (D / 8), col = id % (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[buf][row * KS + col * 8]) = kreg[ch];
+    }
+    if (tid < VBLK) store_transposed_4x8(&Vt[buf][(vdc * 8) * VS + 4 * vkg], VS, vreg[0], vreg[1], vreg[2], vreg[3]);
+  };
+
+  if (nt > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+
+  const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
+  const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
+  for (int kt = 0; kt < nt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nt) gload(kt + 1);
+    const int k0 = kt * BN;
+    const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
+    if (active) {
+      f32x16_t s[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = zero16();
+        const uint16_t* kr = &Ks[buf][(mb * 32 + l32) * KS + g * 8];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(kr + kk * 16));
+          s[mb] = mfma32x32x16(a, qf[kk], s[mb]);
+        }
+      }
+      const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
+      if (need_mask) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
+            const bool ok = key < kl && (!p.causal || key <= qrow);
+            s[mb][j] = ok ? s[mb][j] : NEG_INF_F;
+          }
+      }
+      float mx = NEG_INF_F;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m_run + lazy_thr;
+      if (__any(need)) {
+        const float alpha = need ? fast_exp2((m_run - mx) * c) : 1.f;
+        if (need) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < NMD; ++md)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[md][j] *= alpha;
+      }
+      const float base = (m_run == NEG_INF_F) ? 0.f : m_run * c;
+      float lsum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float pv = fast_exp2(fmaf(s[mb][j], c, -base));
+          s[mb][j] = pv;
+          lsum += pv;
+        }
+      l_run += lsum;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 4; ++kk2) {
+        const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) {
+          const uint16_t* vr = &Vt[buf][(md * 32 + l32) * VS + kk2 * 16 + g * 4];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+          o[md] = mfma32x32x16(as_bf16x8(lo, hi), pb, o[md]);
+        }
+      }
+    }
+    if (kt + 1 < nt) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (qrow < ql) {
+    float inv, lse;
+    if (lt > 0.f) {
+      inv = 1.f / lt;
+      lse = m_run * p.scale + __logf(lt);
+    } else {
+      inv = 0.f;
+      lse = NEG_INF_F;
+    }
+    float* orow = p.o + (long long)(qs + qrow) * p.ld_o + head * D + g * 4;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float4 val = make_float4(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
+                                 o[md][4 * jj + 3] * inv);
+        *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
+      }
+    if (g == 0) p.lse[(long long)head * p.ld_lse + qs + qrow] = lse;
+  }
+}
+
+// Log-sum-exp merge of a step partial into the accumulator (one wavefront
+// covers 64 x 4 consecutive fp32 of a row, i.e. whole heads). `kind` is the
+// partial's step kind (-1: no partial, only the final conversion); rows a
+// step does not cover keep the accumulator. With `final`, every local row is
+// written to the bf16 output: merged values for valid rows, 0 (and lse
+// -inf) for padding rows.
+__global__ void __launch_bounds__(256) lse_merge_kernel(float* __restrict__ acc_o, float* __restrict__ acc_lse,
+                                                        const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_lse,
+                                                        const int32_t* __restrict__ rowflags, int kind, int final_pass,
+                                                        uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                                                        int t_local, int hq, int d, long long ld_lse_out) {
+  const long long q4_per_row = (long long)hq * d / 4;
+  const long long n = (long long)t_local * q4_per_row;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(e / q4_per_row);
+    const int off = (int)(e - (long long)t * q4_per_row) * 4;
+    const int h = off / d;
+    const int f = rowflags[t];
+    const bool valid = f & RF_VALID;
+    const bool covered = kind >= 0 && valid && (kind != 2 || (f & RF_SECOND));
+    if (!covered && !final_pass) continue;
+    float4 oa = make_float4(0.f, 0.f, 0.f, 0.f);
+    float la = NEG_INF_F;
+    if (valid) {
+      oa = *reinterpret_cast<const float4*>(acc_o + (long long)t * hq * d + off);
+      la = acc_lse[(long long)h * t_local + t];
+    }
+    if (covered) {
+      const float4 ob = *reinterpret_cast<const float4*>(part_o + (long long)t * hq * d + off);
+      const float lb = part_lse[(long long)h * t_local + t];
+      const float m = fmaxf(la, lb);
+      float wa = 0.f, wb = 0.f, l = NEG_INF_F;
+      if (m != NEG_INF_F) {
+        wa = __expf(la - m);
+        wb = __expf(lb - m);
+        const float ssum = wa + wb;
+        l = m + __logf(ssum);
+        const float inv = 1.f / ssum;
+        wa *= inv;
+        wb *= inv;
+      }
+      oa = make_float4(wa * oa.x + wb * ob.x, wa * oa.y + wb * ob.y, wa * oa.z + wb * ob.z, wa * oa.w + wb * ob.w);
+      la = l;
+      if (!final_pass) {
+        *reinterpret_cast<float4*>(acc_o + (long long)t * hq * d + off) = oa;
+        // every lane of this (row, head) read acc_lse above: the (row, head)
+        // group is D/4 <= 32 consecutive lanes of one wavefront, whose loads
+        // complete before this store issues
+        if ((off % d) == 0) acc_lse[(long long)h * t_local + t] = l;
+      }
+    }
+    if (final_pass) {
+      uint2 pk;
+      pk.x = pack2_bf16(oa.x, oa.y);
+      pk.y = pack2_bf16(oa.z, oa.w);
+      *reinterpret_cast<uint2*>(out + (long long)t * hq * d + off) = pk;
+      if ((off % d) == 0) lse_out[(long long)h * ld_lse_out + t] = valid ? la : NEG_INF_F;
+    }
+  }
+}
+
+static cp_attn_status launch_fwd_step(const cp_attn_meta* m, int i, const FwdParams& base, int d, int tiles,
+                                      hipStream_t st) {
+  FwdParams p = base;
+  StepTab tb = step_tab(m, i);
+  p.q_start = tb.q_start;
+  p.q_len = tb.q_len;
+  p.kv_start = tb.kv_start;
+  p.kv_len = tb.kv_len;
+  p.items = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
+  p.causal = m->sum.step_kind[i] == 0;
+  const long long blocks = (long long)tiles * p.hq;
+  if (blocks == 0) return CP_ATTN_OK;
+  if (blocks > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
+  if (d == 128)
+    hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hip_check(hipGetLastError(), "fwd_step launch");
+}
+
+static unsigned stream_blocks(long long n, int per_block) {
+  long long b = (n + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  return (unsigned)std::min<long long>(b, 8192);
+}
+
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, int32_t d, int32_t pass) {
+  (void)hkv;
+  if (!m || hq <= 0 || d <= 0) return 0;
+  const size_t tl = (size_t)m->sum.t_local;
+  const size_t o = tl * hq * d * sizeof(float);
+  const size_t l = ((tl * hq * sizeof(float)) + 255) & ~size_t(255);
+  const size_t o_al = (o + 255) & ~size_t(255);
+  if (pass == 0) return 2 * o_al + 2 * l;  // accumulator + step partial (out, lse)
+  return o_al + l;                         // dq accumulator + D = rowsum(dO * O)
+}
+
+static cp_attn_status check_common(const cp_attn_meta* m, const void* q, const void* const* ks, const void* const* vs,
+                                   int hq, int hkv, int d, int causal) {
+  if (!m) return fail(CP_ATTN_ERR_INVALID_ARG, "meta is NULL");
+  if (!q || !ks || !vs) return fail(CP_ATTN_ERR_INVALID_ARG, "NULL tensor argument");
+  if (causal != 1) return fail(CP_ATTN_ERR_UNSUPPORTED, "only causal attention is supported");
+  if (d != 64 && d != 128) return fail(CP_ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return fail(CP_ATTN_ERR_INVALID_ARG, "hq must be a positive multiple of hkv");
+  for (int s = 0; s < m->cp; ++s)
+    if (!ks[s] || !vs[s]) return fail(CP_ATTN_ERR_INVALID_ARG, "NULL K/V shard pointer");
+  if (((uintptr_t)q) & 15) return fail(CP_ATTN_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  for (int s = 0; s < m->cp; ++s)
+    if ((((uintptr_t)ks[s]) | ((uintptr_t)vs[s])) & 15) return fail(CP_ATTN_ERR_INVALID_ARG, "K/V shards must be 16-byte aligned");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != m->device)
+    return fail(CP_ATTN_ERR_INVALID_ARG, "current device differs from the metadata's device");
+  return CP_ATTN_OK;
+}
+
+extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                                      const void* const* v_shards, int32_t hq, int32_t hkv, int32_t d,
+                                      float softmax_scale, int32_t causal, void* out, float* lse, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  set_error("");
+  cp_attn_status rc = check_common(m, q, k_shards, v_shards, hq, hkv, d, causal);
+  if (rc != CP_ATTN_OK) return rc;
+  if (!out || !lse) return fail(CP_ATTN_ERR_INVALID_ARG, "NULL output");
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f)) return fail(CP_ATTN_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  if (((uintptr_t)out) & 15) return fail(CP_ATTN_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  const size_t need = cp_attn_workspace_bytes(m, hq, hkv, d, 0);
+  if (!workspace || ws_bytes < need) return fail(CP_ATTN_ERR_WORKSPACE, "forward workspace missing or too small");
+  if (((uintptr_t)workspace) & 255) return fail(CP_ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int tl = m->sum.t_local;
+  if (tl == 0) return CP_ATTN_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
+  const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);
+  char* ws = (char*)workspace;
+  float* acc_o = (float*)ws;
+  float* part_o = (float*)(ws + o_al);
+  float* acc_l = (float*)(ws + 2 * o_al);
+  float* part_l = (float*)(ws + 2 * o_al + l_al);
+  const int32_t* rowflags = m->d_tab + m->lay.rowflags;
+
+  FwdParams base{};
+  base.q = (const uint16_t*)q;
+  base.hq = hq;
+  base.group = hq / hkv;
+  base.ld_q = (long long)hq * d;
+  base.ld_kv = (long long)hkv * d;
+  base.scale = softmax_scale;
+  base.c_log2 = softmax_scale * LOG2E_F;
+  base.ld_o = (long long)hq * d;
+  base.ld_lse = tl;
+  const long long n4 = (long long)tl * hq * d / 4;
+  for (int i = 0; i < m->cp; ++i) {
+    const int s = m->sum.step_src[i];
+    FwdParams p = base;
+    p.k = (const uint16_t*)k_shards[s];
+    p.v = (const uint16_t*)v_shards[s];
+    p.o = (i == 0) ? acc_o : part_o;
+    p.lse = (i == 0) ? acc_l : part_l;
+    rc = launch_fwd_step(m, i, p, d, (int)m->sum.tiles_fwd[i], st);
+    if (rc != CP_ATTN_OK) return rc;
+    if (i >= 1) {
+      hipLaunchKernelGGL(lse_merge_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, acc_o, acc_l, part_o,
+                         part_l, rowflags, m->sum.step_kind[i], (i == m->cp - 1) ? 1 : 0, (uint16_t*)out, lse, tl, hq,
+                         d, (long long)m->t_alloc);
+      rc = hip_check(hipGetLastError(), "lse_merge launch");
+      if (rc != CP_ATTN_OK) return rc;
+    }
+  }
+  if (m->cp == 1) {
+    hipLaunchKernelGGL(lse_merge_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, acc_o, acc_l, part_o, part_l,
+                       rowflags, -1, 1, (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
+    rc = hip_check(hipGetLastError(), "lse_merge launch");
+  }
+  return rc;
+}

@@ -1,0 +1,107 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// MFMA used throughout: v_mfma_f32_32x32x16_bf16 (one wavefront of 64 lanes).
+// Operand layouts, with lane = 32 * g + i (g = 0/1, i = 0..31):
+//   A (32 x 16, row-major M x K): lane holds row i, k = 8g .. 8g+7
+//   B (16 x 32, K x N):          lane holds column i, k = 8g .. 8g+7
+//   C (32 x 32 fp32, 16 values): lane holds column i, rows
+//                                8*(j/4) + 4*g + (j%4), j = 0..15
+// Because the contraction runs over k, any permutation of k applied to both
+// A and B leaves the product unchanged. The kernels use this to feed a C
+// fragment (lane = one column, 16 rows) straight back as a B operand: the
+// eight values j = 8h .. 8h+7 of a C fragment are the "k = 8g..8g+7" of the
+// 16-wide slice h, which pairs with A rows read at the matching positions
+// 16h + 4g + {0,1,2,3} and 16h + 8 + 4g + {0,1,2,3}.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float NEG_INF_F = -__builtin_huge_valf();
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) z[j] = 0.f;
+  return z;
+}
+
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint2& lo, const uint2& hi) {
+  uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Eight consecutive fp32 values of a C fragment -> bf16 B operand.
+__device__ __forceinline__ bf16x8_t pack8_bf16(const f32x16_t& c, int j0) {
+  uint4 u;
+  u.x = pack2_bf16(c[j0 + 0], c[j0 + 1]);
+  u.y = pack2_bf16(c[j0 + 2], c[j0 + 3]);
+  u.z = pack2_bf16(c[j0 + 4], c[j0 + 5]);
+  u.w = pack2_bf16(c[j0 + 6], c[j0 + 7]);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 halves of two dwords -> one dword (lo from a, hi from b), selected half
+__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& u, int w) {
+  return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
+}
+
+// Transpose a 4 (rows) x 8 (cols) bf16 block held as four 16-byte rows into
+// eight 4-element columns, written as 8-byte LDS stores to dst + e * stride.
+__device__ __forceinline__ void store_transposed_4x8(uint16_t* dst, int stride, const uint4& r0, const uint4& r1,
+                                                     const uint4& r2, const uint4& r3) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t a0 = u4_get(r0, w), a1 = u4_get(r1, w), a2 = u4_get(r2, w), a3 = u4_get(r3, w);
+    uint2 ev = make_uint2(pick_lo(a0, a1), pick_lo(a2, a3));
+    uint2 od = make_uint2(pick_hi(a0, a1), pick_hi(a2, a3));
+    *reinterpret_cast<uint2*>(dst + (2 * w) * stride) = ev;
+    *reinterpret_cast<uint2*>(dst + (2 * w + 1) * stride) = od;
+  }
+}
+
+// Block -> (work item, head). When the head count is a multiple of the 8
+// XCDs, the blocks that land on one XCD (consecutive ids are dealt to the
+// XCDs round-robin) take a contiguous run of heads, so a GQA group's K/V stay
+// in one XCD's L2.
+__device__ __forceinline__ void map_block(int bid, int nheads, int& item, int& head) {
+  if ((nheads & 7) == 0) {
+    const int per = nheads >> 3;
+    const int xcd = bid & 7;
+    const int r = bid >> 3;
+    head = xcd * per + (r % per);
+    item = r / per;
+  } else {
+    item = bid / nheads;
+    head = bid - item * nheads;
+  }
+}
+
+}  // namespace cpattn

@@ -1,0 +1,203 @@
+/*
+ * cp_attn.h - one context-parallel rank's share of packed variable-length
+ * ("thd") causal attention with ring (P2P) KV exchange, on one MI355X (gfx950).
+ *
+ * The pages this follows (cited by title and section):
+ *  [I1]  "thd format is not supported with hierarchical CP implementation yet"
+ *        (Transformer Engine issue 2208): packed THD sequences, the P2P ring
+ *        and the a2a / a2a+p2p communication types; P2P suits long sequences
+ *        because the ring exchange can hide under compute.
+ *  [I2]  "[PyTorch][Attention] THD P2P context-parallel regression when padded
+ *        cu_seqlens are value-equal but not object-identical" (Transformer
+ *        Engine issue 3487), sections "Describe the bug", "Steps/Code to
+ *        reproduce bug" and "Expected behavior": cu_seqlens / padded
+ *        cu_seqlens, the automatic pad_between_seqs decision (which must be
+ *        taken from values, not object identity), per-rank sequence lengths
+ *        recomputed per ring step, THD dQ/dK/dV tail zeroing that should only
+ *        run when a tail exists, and graph-safe padding metadata.
+ *  [I3]  "Hybrid / Hierarchical Context Parallel Skill", sections
+ *        "Enablement" and "Code Anchors": every sequence length must divide
+ *        by 2*CP; hierarchical sizes are [a2a size, p2p size] whose product is
+ *        CP.
+ *
+ * Conventions used by every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says "host".
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - bf16 tensors are row-major [rows, heads, head_dim]; a rank's local
+ *    tensors hold t_alloc >= T_local rows (T_local = cu_seqlens_padded[B]/CP).
+ *  - LSE is the natural-log log-sum-exp of the scaled scores, fp32, laid out
+ *    [heads, t_alloc] (head-major).
+ *  - Local row layout of rank r (and of every KV shard s, with s in place of
+ *    r): sequence b occupies local rows [cup[b]/CP, cup[b+1]/CP); the first
+ *    half of that slot is chunk r of the sequence's 2*CP chunks and the second
+ *    half is chunk 2*CP-1-r (the load-balanced pairing). Valid tokens fill
+ *    chunks in order; padding sits at the end of a sequence's padded slot.
+ *  - Every call returns a cp_attn_status. On failure nothing further is
+ *    launched and cp_attn_last_error() (thread-local) describes the cause.
+ *    Faults of earlier asynchronous work surface as CP_ATTN_ERR_HIP.
+ *  - Caller owns every tensor and workspace; the library owns only the
+ *    cp_attn_meta handle (device tables plus a pinned summary).
+ */
+#ifndef CP_ATTN_H_
+#define CP_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CP_ATTN_OK = 0,
+  CP_ATTN_ERR_INVALID_ARG = 1,   /* bad sizes / pointers / layout rules */
+  CP_ATTN_ERR_UNSUPPORTED = 2,   /* e.g. head_dim not 64/128, non-causal */
+  CP_ATTN_ERR_HINT_MISMATCH = 3, /* pad_hint contradicts the values */
+  CP_ATTN_ERR_WORKSPACE = 4,     /* workspace missing or too small */
+  CP_ATTN_ERR_HIP = 5            /* a HIP runtime call failed */
+} cp_attn_status;
+
+#define CP_ATTN_MAX_CP 16
+
+/* Opaque per-batch metadata handle (device tables + host summary). */
+typedef struct cp_attn_meta cp_attn_meta;
+
+/* Host-side summary of a metadata handle. step_kind[i]: 0 = own shard, causal
+ * on local rows; 1 = source shard s < rank: all query rows x the first half of
+ * shard s, no mask; 2 = s > rank: second-half query rows x all of shard s, no
+ * mask. step_src[i] = (rank - i) mod CP. tiles_* are the per-step work-item
+ * counts of the forward / dQ kernels and of the dK/dV kernel. */
+typedef struct {
+  int32_t B, cp_size, cp_rank;
+  int32_t pad_between_seqs; /* 1 iff cu_seqlens != cu_seqlens_padded anywhere (by value) */
+  int32_t t_local;          /* cu_seqlens_padded[B] / CP */
+  int32_t has_tail;         /* 1 iff t_alloc > t_local */
+  int64_t t_alloc;
+  int32_t step_kind[CP_ATTN_MAX_CP];
+  int32_t step_src[CP_ATTN_MAX_CP];
+  int64_t tiles_fwd[CP_ATTN_MAX_CP];
+  int64_t tiles_dkdv[CP_ATTN_MAX_CP];
+  int64_t valid_rows;       /* valid (non-padding) local rows of this rank */
+} cp_attn_summary;
+
+/*
+ * Build rank cp_rank's per-batch metadata on the device (one small kernel
+ * group, then ONE host synchronisation to read back a <1 KB summary; the only
+ * synchronisation in the library). [I2] "Describe the bug": the per-step
+ * per-rank cu_seqlens; [I2] "Expected behavior": the padding decision is
+ * taken from values only - the library never compares pointers, so an
+ * aliased, NULL or distinct-but-equal cu_seqlens_padded all yield identical
+ * tables and the same kernel sequence. [I3] "Enablement": padded lengths must
+ * divide by 2*CP.
+ *
+ *  cu_seqlens         device int32 [B+1], cu[0] = 0, non-decreasing (valid lengths)
+ *  cu_seqlens_padded  device int32 [B+1] (padded lengths); may alias cu_seqlens;
+ *                     NULL means "no padding" (= cu_seqlens)
+ *  B                  number of sequences, >= 1
+ *  cp_size, cp_rank   ring size (1..CP_ATTN_MAX_CP) and this rank
+ *  pad_hint           -1 = decide from the values; 0 / 1 = caller asserts
+ *                     no padding / padding; a contradiction with the values
+ *                     returns CP_ATTN_ERR_HINT_MISMATCH
+ *  t_alloc            rows allocated in this rank's local tensors (>= T_local)
+ *  out                receives the handle (free with cp_attn_meta_free)
+ * Device-side checks (reported after the sync): cu[0] = cup[0] = 0, both
+ * non-decreasing, 0 <= L_b <= P_b, P_b % (2*CP) == 0, t_alloc >= T_local.
+ */
+cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded,
+                                     int32_t B, int32_t cp_size, int32_t cp_rank, int32_t pad_hint,
+                                     int64_t t_alloc, void* stream, cp_attn_meta** out);
+
+/* Copy the host summary (no device work). */
+cp_attn_status cp_attn_meta_summary(const cp_attn_meta* m, cp_attn_summary* out);
+
+/*
+ * Export the integer tables to a host buffer (synchronous device->host copy;
+ * for tests and tooling). Layout, all int32, in this order:
+ *   header[8] = {B, CP, rank, pad_between_seqs, T_local, has_tail, n_steps=CP, 0}
+ *   chunk[B]                       c_b = P_b / (2 CP)
+ *   cu_padded_local[B+1]           cup / CP
+ *   cu_padded_half[B+1]            cup / (2 CP)
+ *   for s in 0..CP-1: cu_full_s[B+1], cu_first_s[B+1], cu_second_s[B+1]
+ *                                  exclusive prefix sums of the valid rows of
+ *                                  shard s (both chunks / first / second chunk)
+ *   for i in 0..CP-1: {kind, src}, q_start[B], q_len[B], kv_start[B], kv_len[B]
+ *                                  step i's query and key row ranges in local rows
+ * n is the capacity of host_buf in int32 elements; *n_needed receives the
+ * required count (call with host_buf = NULL to query).
+ */
+cp_attn_status cp_attn_meta_export(const cp_attn_meta* m, int32_t* host_buf, size_t n, size_t* n_needed);
+
+/* Release the handle (synchronises the device it was built on). NULL is a no-op. */
+void cp_attn_meta_free(cp_attn_meta* m);
+
+/* Workspace bytes needed by cp_attn_fwd (pass 0) or cp_attn_bwd (pass 1). */
+size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, int32_t d, int32_t pass);
+
+/*
+ * Forward of the rank's share: for ring step i = 0..CP-1 the step's query
+ * rows attend to the step's key rows of shard s = (rank - i) mod CP (one
+ * flash-style MFMA kernel per step, causal on local rows at step 0 only),
+ * and the per-step partial outputs are folded through their log-sum-exp.
+ * [I1] the P2P ring; [I2] "Describe the bug": per-step metadata.
+ *
+ *  q                  bf16 [t_alloc, hq, d]: this rank's query rows
+ *  k_shards, v_shards HOST arrays of CP device pointers, bf16 [t_alloc, hkv, d];
+ *                     entry s is the shard of rank s (entry rank = own K/V)
+ *  hq, hkv, d         heads (hq % hkv == 0; query head h uses KV head h/(hq/hkv)),
+ *                     head_dim in {64, 128}
+ *  softmax_scale      multiplies q.k (usually 1/sqrt(d))
+ *  causal             must be 1
+ *  out                bf16 [t_alloc, hq, d]: rows [0, T_local) written; padding
+ *                     rows are 0; rows >= T_local untouched
+ *  lse                fp32 [hq, t_alloc]: natural-log LSE, padding rows -inf,
+ *                     columns >= T_local untouched
+ *  workspace          device scratch of cp_attn_workspace_bytes(m, .., 0) bytes
+ * Never synchronises; capturable in a HIP graph.
+ */
+cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                           const void* const* v_shards, int32_t hq, int32_t hkv, int32_t d,
+                           float softmax_scale, int32_t causal, void* out, float* lse,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the rank's share: the gradient of sum(dout * out) with respect
+ * to this rank's queries (dq) and to every source shard's keys and values
+ * (dk_parts[s], dv_parts[s]: the contribution of this rank's query rows only,
+ * in shard s's local layout; in a real ring these are what travels back).
+ * THD gradient tail zeroing ([I2] "Describe the bug" and "Expected
+ * behavior"): rows [T_local, t_alloc) of dq and of every part are zeroed by
+ * one extra launch, made only when the metadata shows such a tail exists.
+ *
+ *  q, k_shards, v_shards, hq, hkv, d, softmax_scale, causal: as cp_attn_fwd
+ *  out, lse           the forward's outputs
+ *  dout               bf16 [t_alloc, hq, d]
+ *  dq                 bf16 [t_alloc, hq, d] (overwritten; padding rows 0)
+ *  dk_parts, dv_parts HOST arrays of CP device pointers, bf16 [t_alloc, hkv, d]
+ *                     (overwritten; rows outside the step's key range 0)
+ *  workspace          device scratch of cp_attn_workspace_bytes(m, .., 1) bytes
+ * Never synchronises; capturable in a HIP graph.
+ */
+cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                           const void* const* v_shards, const void* out, const float* lse,
+                           const void* dout, int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
+                           int32_t causal, void* dq, void* const* dk_parts, void* const* dv_parts,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Data-loader helper: gather the rows that rank `shard` holds out of a global
+ * packed tensor (rows in cu_seqlens_padded order) into that rank's local
+ * layout (see the conventions above). row_bytes = heads * head_dim * element
+ * size, a multiple of 16. `global` has cu_seqlens_padded[B] rows; `local` has
+ * T_local rows (rows >= T_local are not touched). [I3] "Enablement" (2*CP
+ * chunks) with the load-balanced pairing of chunks k and 2*CP-1-k.
+ */
+cp_attn_status cp_attn_shard_gather(const cp_attn_meta* m, int32_t shard, const void* global,
+                                    void* local, size_t row_bytes, void* stream);
+
+/* Thread-local description of the last failure ("" if none). */
+const char* cp_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CP_ATTN_H_ */

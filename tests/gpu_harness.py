@@ -1,0 +1,170 @@
+"""Test-side helpers: run the HIP path through the C ABI and compare with the oracle.
+
+Inputs reach the device as global packed bf16 tensors; the library's own
+shard gather builds the rank-local layout. The oracle computes from the same
+global arrays on the CPU. Nothing here is shared with the library.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+from context_packed_attention_amd import api
+
+OUT_ATOL = 2e-2      # max-abs on bf16 outputs (out, dQ, dK, dV)
+OUT_REL_L2 = 1e-2    # relative L2 on the same tensors
+LSE_REL = 1e-3       # |dlse| <= 1e-3 * max(1, |lse|)
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return t.view(torch.bfloat16)
+
+
+def dev_i32(a):
+    import torch
+    return torch.tensor(np.asarray(a, dtype=np.int32), dtype=torch.int32, device="cuda")
+
+
+def bf16_to_np(t) -> np.ndarray:
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def parse_export(arr: np.ndarray) -> dict:
+    """Split the flat int32 export (layout documented in cp_attn.h)."""
+    a = [int(x) for x in arr]
+    B, cp, rank, pad, tl, tail, nst = a[:7]
+    o = 8
+    md = {"B": B, "cp": cp, "rank": rank, "pad_between_seqs": pad, "t_local": tl, "has_tail": tail}
+
+    def take(n):
+        nonlocal o
+        v = a[o:o + n]
+        o += n
+        return v
+
+    md["chunk"] = take(B)
+    md["cu_padded_local"] = take(B + 1)
+    md["cu_padded_half"] = take(B + 1)
+    for s in range(cp):
+        md[f"cu_full_{s}"] = take(B + 1)
+        md[f"cu_first_{s}"] = take(B + 1)
+        md[f"cu_second_{s}"] = take(B + 1)
+    steps = []
+    for _ in range(nst):
+        kind, src = take(2)
+        steps.append({"kind": kind, "src": src, "q_start": take(B), "q_len": take(B),
+                      "kv_start": take(B), "kv_len": take(B)})
+    md["steps"] = steps
+    assert o == len(a)
+    return md
+
+
+class DeviceBatch:
+    """Global packed tensors of a batch, resident on the GPU."""
+
+    def __init__(self, batch):
+        self.batch = batch
+        self.q = dev_bf16(batch.q)
+        self.k = dev_bf16(batch.k)
+        self.v = dev_bf16(batch.v)
+        self.do = dev_bf16(batch.do)
+        self.cu = dev_i32(batch.cu)
+        self.cup = dev_i32(batch.cup)   # a distinct tensor with (maybe) equal values
+
+
+def local_inputs(db: DeviceBatch, cp: int, rank: int, tail: int = 0, pad_hint: int = -1, cup="copy",
+                 garbage: float | None = None):
+    """Metadata + rank-local tensors (q, dO of `rank`; K/V of every shard)."""
+    import torch
+    bt = db.batch
+    T_local = int(bt.cup[-1]) // cp
+    t_alloc = T_local + tail
+    cup_arg = {"copy": db.cup, "alias": db.cu, "null": None}[cup]
+    meta = api.cp_attn_rank_metadata(db.cu, cup_arg, cp, rank, pad_hint, t_alloc)
+
+    def alloc(h):
+        if garbage is None:
+            return torch.zeros((t_alloc, h, bt.d), dtype=torch.bfloat16, device="cuda")
+        return torch.full((t_alloc, h, bt.d), garbage, dtype=torch.bfloat16, device="cuda")
+
+    def gather(src, h, shard):
+        dst = alloc(h)
+        api.cp_attn_shard_gather(meta, shard, src, dst, h * bt.d * 2)
+        return dst
+
+    q = gather(db.q, bt.hq, rank)
+    do = gather(db.do, bt.hq, rank)
+    ks = [gather(db.k, bt.hkv, s) for s in range(cp)]
+    vs = [gather(db.v, bt.hkv, s) for s in range(cp)]
+    return meta, {"q": q, "do": do, "k": ks, "v": vs, "t_alloc": t_alloc, "t_local": T_local}
+
+
+def run_fwd(meta, loc, bt, scale):
+    import torch
+    t_alloc = loc["t_alloc"]
+    out = torch.full((t_alloc, bt.hq, bt.d), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((bt.hq, t_alloc), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.cp_attn_workspace_bytes(meta, bt.hq, bt.hkv, bt.d, 0), dtype=torch.uint8, device="cuda")
+    api.cp_attn_fwd(meta, loc["q"], loc["k"], loc["v"], bt.hq, bt.hkv, bt.d, scale, 1, out, lse, ws)
+    return out, lse
+
+
+def run_bwd(meta, loc, bt, scale, out, lse, garbage: float = 5.0):
+    import torch
+    t_alloc = loc["t_alloc"]
+    cp = meta.cp
+    dq = torch.full((t_alloc, bt.hq, bt.d), garbage, dtype=torch.bfloat16, device="cuda")
+    dks = [torch.full((t_alloc, bt.hkv, bt.d), garbage, dtype=torch.bfloat16, device="cuda") for _ in range(cp)]
+    dvs = [torch.full((t_alloc, bt.hkv, bt.d), garbage, dtype=torch.bfloat16, device="cuda") for _ in range(cp)]
+    ws = torch.empty(api.cp_attn_workspace_bytes(meta, bt.hq, bt.hkv, bt.d, 1), dtype=torch.uint8, device="cuda")
+    api.cp_attn_bwd(meta, loc["q"], loc["k"], loc["v"], out, lse, loc["do"], bt.hq, bt.hkv, bt.d, scale, 1,
+                    dq, dks, dvs, ws)
+    return dq, dks, dvs
+
+
+def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None):
+    """A17/A16-style check: max-abs <= 2e-2 (or one bf16 ulp of the reference
+    where |ref| >= 8) and relative L2 <= 1e-2. Returns a stats dict."""
+    got = bf16_bits_to_f64(got_bits)
+    if rows is not None:
+        got = got[rows]
+        ref = ref[rows]
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    err = np.abs(got - ref)
+    big = np.abs(ref) >= 8.0
+    ulp = np.where(big, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 7), 0.0)
+    tol = np.maximum(OUT_ATOL, ulp)
+    worst = float((err / tol).max()) if err.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))
+    st = {"max_abs": float(err.max()) if err.size else 0.0, "worst_over_tol": worst, "rel_l2": rel,
+          "max_ref": float(np.abs(ref).max()) if ref.size else 0.0}
+    assert worst <= 1.0, f"{name}: max-abs {st['max_abs']:.3e} exceeds tolerance ({st})"
+    assert rel <= OUT_REL_L2 or nref == 0.0, f"{name}: relative L2 {rel:.3e} > {OUT_REL_L2} ({st})"
+    return st
+
+
+def compare_lse(name: str, got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), ~fin), f"{name}: -inf pattern differs"
+    d = np.abs(got[fin] - ref[fin])
+    tol = LSE_REL * np.maximum(1.0, np.abs(ref[fin]))
+    worst = float((d / tol).max()) if d.size else 0.0
+    assert worst <= 1.0, f"{name}: lse error {d.max():.3e} over tolerance"
+    return {"max_abs": float(d.max()) if d.size else 0.0, "worst_over_tol": worst}
