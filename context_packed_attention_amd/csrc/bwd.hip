@@ -1,7 +1,444 @@
-// Backward of one CP rank's share (filled in below).
+// Backward of one CP rank's share on MFMA.
+//
+// Per ring step (the same step tables as the forward): a dK/dV kernel whose
+// blocks own 128 key rows of the source shard and loop over the step's query
+// rows (and over the query heads of a GQA group), and a dQ kernel whose blocks
+// own 128 query rows and loop over the step's key rows. Both recompute the
+// probabilities from the forward's final LSE, P = exp(scale q.k - lse), and
+// use dS = P (dP - D) with D = rowsum(dO * out). THD gradient tail zeroing
+// ("[PyTorch][Attention] THD P2P context-parallel regression ...", sections
+// "Describe the bug" and "Expected behavior") is one extra launch made only
+// when the metadata reports rows past the valid end (t_alloc > T_local).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "internal.h"
+#include "kern_common.h"
+
+namespace cpattn {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;   // forward LSE [hq, ld_lse]
+  const float* dvec;  // D = rowsum(dO * out) [hq, ld_d]
+  long long ld_lse, ld_d;
+  const int32_t* q_start;
+  const int32_t* q_len;
+  const int32_t* kv_start;
+  const int32_t* kv_len;
+  const int32_t* slot;   // cu_seqlens_padded / CP (slot starts, B + 1)
+  const int32_t* items;  // (sequence, tile) pairs
+  int hq, hkv, group;
+  long long ld_q, ld_kv;
+  float scale, c_log2;
+  int causal;
+  float* dq_acc;   // fp32 [T_local, hq, D]
+  int dq_first;    // 1: store, 0: accumulate
+  uint16_t* dk;    // bf16 [t_alloc, hkv, D] part of the source shard
+  uint16_t* dv;
+};
+
+// D = rowsum(dO * out) per (row, head), fp32 [hq, t_local]; 0 on padding rows.
+// 16 lanes cover one (row, head) of D = 128 (8 lanes for D = 64).
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ out,
+                                                      const int32_t* __restrict__ rowflags, float* __restrict__ dvec,
+                                                      int t_local, int hq, int d) {
+  const int lanes = d / 8;
+  const long long n = (long long)t_local * hq * lanes;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
+    const long long rh = e / lanes;
+    const int part = (int)(e - rh * lanes);
+    const int t = (int)(rh / hq);
+    const int h = (int)(rh - (long long)t * hq);
+    float acc = 0.f;
+    if (rowflags[t] & RF_VALID) {
+      const uint4 a = *reinterpret_cast<const uint4*>(dout + rh * d + part * 8);
+      const uint4 b = *reinterpret_cast<const uint4*>(out + rh * d + part * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = u4_get(a, w), y = u4_get(b, w);
+        acc += __uint_as_float(x << 16) * __uint_as_float(y << 16);
+        acc += __uint_as_float(x & 0xffff0000u) * __uint_as_float(y & 0xffff0000u);
+      }
+    }
+    for (int off = lanes >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (part == 0) dvec[(long long)h * t_local + t] = acc;
+  }
+}
+
+// dQ of one ring step. Block = 4 wavefronts x 32 query rows of one head; key
+// tiles of 32 rows are staged in LDS three ways (K and V row-major for the
+// transposed scores S^T = K Q^T and dP^T = V dO^T, and K^T for dQ^T = K^T dS^T),
+// double-buffered: half the threads fetch K, the other half V.
+template <int D>
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
+  constexpr int BM = FWD_BM, BN = 32;
+  constexpr int KS = D + 8, TS = BN + 4;
+  constexpr int NKK = D / 16, NMD = D / 32;
+  constexpr int NB = (BN / 4) * (D / 8);  // 4x8 blocks per tile and tensor
+  static_assert(NB <= 128, "K blocks on threads [0,128), V blocks on [128,256)");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  int item, head;
+  map_block(blockIdx.x, p.hq, item, head);
+  const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
+  const int qs = p.q_start[sb], ql = p.q_len[sb], kvs = p.kv_start[sb], kl = p.kv_len[sb];
+  const int q0 = tile * BM;
+  const int nq = min(BM, ql - q0);
+  const int kvh = head / p.group;
+  const int n_keys = p.causal ? min(kl, q0 + nq) : kl;
+  const int nt = (n_keys + BN - 1) / BN;
+  const float c = p.c_log2;
+
+  const int qrow = q0 + w * 32 + l32;
+  const bool qok = qrow < ql;
+  bf16x8_t qf[NKK], df[NKK];
+  {
+    const long long roff = (long long)(qs + (qok ? qrow : 0)) * p.ld_q + head * D + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p.q + roff + kk * 16) : make_uint4(0, 0, 0, 0));
+      df[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p.dout + roff + kk * 16) : make_uint4(0, 0, 0, 0));
+    }
+  }
+  const float lse2 = qok ? p.lse[(long long)head * p.ld_lse + qs + qrow] * LOG2E_F : __builtin_huge_valf();
+  const float dq_d = qok ? p.dvec[(long long)head * p.ld_d + qs + qrow] : 0.f;
+
+  f32x16_t acc[NMD];
+#pragma unroll
+  for (int md = 0; md < NMD; ++md) acc[md] = zero16();
+
+  const bool is_k = tid < NB, is_v = tid >= 128 && tid < 128 + NB;
+  const int blk = is_k ? tid : tid - 128;
+  const int kg = blk / (D / 8), dc = blk % (D / 8);
+  const uint16_t* src = (is_k ? p.k : p.v) + (long long)kvs * p.ld_kv + kvh * D + dc * 8;
+  uint4 rg[4];
+
+  auto gload = [&](int kt) {
+    if (is_k || is_v) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt * BN + 4 * kg + r;
+        rg[r] = key < kl ? *reinterpret_cast<const uint4*>(src + (long long)key * p.ld_kv) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+    if (is_k || is_v) {
+      uint16_t* rm = is_k ? Ks[buf] : Vs[buf];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&rm[(4 * kg + r) * KS + dc * 8]) = rg[r];
+      if (is_k) store_transposed_4x8(&Kt[buf][(dc * 8) * TS + 4 * kg], TS, rg[0], rg[1], rg[2], rg[3]);
+    }
+  };
+
+  if (nt > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
+  for (int kt = 0; kt < nt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nt) gload(kt + 1);
+    const int k0 = kt * BN;
+    const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
+    if (active) {
+      f32x16_t s = zero16(), dp = zero16();
+      const uint16_t* krow = &Ks[buf][l32 * KS + g * 8];
+      const uint16_t* vrow = &Vs[buf][l32 * KS + g * 8];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(krow + kk * 16)), qf[kk], s);
+        dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + kk * 16)), df[kk], dp);
+      }
+      const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float pv = fast_exp2(fmaf(s[j], c, -lse2));
+        if (need_mask) {
+          const int key = k0 + (j >> 2) * 8 + g * 4 + (j & 3);
+          const bool ok = key < kl && (!p.causal || key <= qrow);
+          pv = ok ? pv : 0.f;
+        }
+        s[j] = pv * (dp[j] - dq_d);  // dS^T
+      }
+#pragma unroll
+      for (int kk2 = 0; kk2 < BN / 16; ++kk2) {
+        const bf16x8_t ds = pack8_bf16(s, 8 * kk2);
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) {
+          const uint16_t* tr = &Kt[buf][(md * 32 + l32) * TS + kk2 * 16 + g * 4];
+          const uint2 lo = *reinterpret_cast<const uint2*>(tr);
+          const uint2 hi = *reinterpret_cast<const uint2*>(tr + 8);
+          acc[md] = mfma32x32x16(as_bf16x8(lo, hi), ds, acc[md]);
+        }
+      }
+    }
+    if (kt + 1 < nt) swrite(buf ^ 1);
+    __syncthreads();
+  }
+  if (qok) {
+    float* dst = p.dq_acc + (long long)(qs + qrow) * p.hq * D + head * D + g * 4;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float4 val = make_float4(acc[md][4 * jj] * p.scale, acc[md][4 * jj + 1] * p.scale,
+                                 acc[md][4 * jj + 2] * p.scale, acc[md][4 * jj + 3] * p.scale);
+        float4* ptr = reinterpret_cast<float4*>(dst + md * 32 + jj * 8);
+        if (!p.dq_first) {
+          const float4 old = *ptr;
+          val.x += old.x;
+          val.y += old.y;
+          val.z += old.z;
+          val.w += old.w;
+        }
+        *ptr = val;
+      }
+  }
+}
+
+// dK/dV of one ring step for the source shard's key rows. Block = 4
+// wavefronts x 32 key rows of one KV head (DKDV_BN = 128 keys); loops over the
+// query heads of the group and the step's query rows in tiles of 32. Q and dO
+// tiles are staged in LDS row-major (scores S = Q K^T, dP = dO V^T) and
+// transposed (dK^T = Q^T dS, dV^T = dO^T P), double-buffered.
+// Rows of the part outside the step's key range are written as zeros, so the
+// whole shard-s part is defined after the step.
+template <int D>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BK = DKDV_BN, BQ = 32;
+  constexpr int QS = D + 8, TS = BQ + 4;
+  constexpr int NKK = D / 16, NMD = D / 32;
+  constexpr int NB = (BQ / 4) * (D / 8);  // 4x8 blocks per q tile and tensor
+  static_assert(2 * NB <= 256, "one block per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TS];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Dv[2][BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  int item, kvh;
+  map_block(blockIdx.x, p.hkv, item, kvh);
+  const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
+  const int qs = p.q_start[sb], ql = p.q_len[sb], kvs = p.kv_start[sb], kl = p.kv_len[sb];
+  const int slot_len = p.slot[sb + 1] - p.slot[sb];
+  const int k0 = tile * BK;
+  const int rows_here = min(BK, slot_len - k0);
+  const int nk = max(0, min(BK, kl - k0));
+  const int key = k0 + w * 32 + l32;  // this lane's key row (relative to the slot)
+  const float c = p.c_log2;
+
+  f32x16_t dk[NMD], dv[NMD];
+#pragma unroll
+  for (int md = 0; md < NMD; ++md) {
+    dk[md] = zero16();
+    dv[md] = zero16();
+  }
+
+  // query tiles to visit: causal steps skip tiles entirely before this key tile
+  const int qt_begin = (p.causal && nk > 0) ? (k0 / BQ) : 0;
+  const int qt_end = nk > 0 ? (ql + BQ - 1) / BQ : 0;
+  const int n_qt = max(0, qt_end - qt_begin);
+  const int n_iter = n_qt * p.group;
+
+  if (n_iter > 0) {
+    bf16x8_t kf[NKK], vf[NKK];
+    {
+      const bool ok = key < kl;
+      const long long off = (long long)(kvs + (ok ? key : 0)) * p.ld_kv + kvh * D + g * 8;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.k + off + kk * 16) : make_uint4(0, 0, 0, 0));
+        vf[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.v + off + kk * 16) : make_uint4(0, 0, 0, 0));
+      }
+    }
+    uint4 rg[4];
+    float lval = 0.f;
+    const bool is_q = tid < NB, is_d = tid >= 128 && tid < 128 + NB;
+    const int blk = is_q ? tid : tid - 128;
+    const int qg = blk / (D / 8), dc = blk % (D / 8);
+
+    auto gload = [&](int it) {
+      const int hh = kvh * p.group + it / n_qt;
+      const int qt = qt_begin + it % n_qt;
+      if (is_q || is_d) {
+        const uint16_t* src = is_q ? p.q : p.dout;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qrow = qt * BQ + 4 * qg + r;
+          rg[r] = qrow < ql ? *reinterpret_cast<const uint4*>(src + (long long)(qs + qrow) * p.ld_q + hh * D + dc * 8)
+                            : make_uint4(0, 0, 0, 0);
+        }
+      }
+      if (tid >= 64 && tid < 64 + BQ) {
+        const int qrow = qt * BQ + tid - 64;
+        lval = qrow < ql ? p.lse[(long long)hh * p.ld_lse + qs + qrow] * LOG2E_F : __builtin_huge_valf();
+      } else if (tid >= 192 && tid < 192 + BQ) {
+        const int qrow = qt * BQ + tid - 192;
+        lval = qrow < ql ? p.dvec[(long long)hh * p.ld_d + qs + qrow] : 0.f;
+      }
+    };
+    auto swrite = [&](int buf) {
+      if (is_q || is_d) {
+        uint16_t* rm = is_q ? Qs[buf] : Ds[buf];
+        uint16_t* tm = is_q ? Qt[buf] : Dt[buf];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&rm[(4 * qg + r) * QS + dc * 8]) = rg[r];
+        store_transposed_4x8(&tm[(dc * 8) * TS + 4 * qg], TS, rg[0], rg[1], rg[2], rg[3]);
+      }
+      if (tid >= 64 && tid < 64 + BQ) Ls[buf][tid - 64] = lval;
+      else if (tid >= 192 && tid < 192 + BQ) Dv[buf][tid - 192] = lval;
+    };
+
+    gload(0);
+    swrite(0);
+    __syncthreads();
+    const int wkey_lo = k0 + w * 32, wkey_hi = wkey_lo + 31;
+    for (int it = 0; it < n_iter; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < n_iter) gload(it + 1);
+      const int qt = qt_begin + it % n_qt;
+      const int qlo = qt * BQ, qhi = qlo + BQ - 1;
+      const bool active = wkey_lo < kl && !(p.causal && qhi < wkey_lo);
+      if (active) {
+        // S = Q K^T and dP = dO V^T: rows q (this lane: 16 of them), column key
+        f32x16_t s = zero16(), dp = zero16();
+        const uint16_t* qrow_p = &Qs[buf][l32 * QS + g * 8];
+        const uint16_t* drow_p = &Ds[buf][l32 * QS + g * 8];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          s = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(qrow_p + kk * 16)), kf[kk], s);
+          dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(drow_p + kk * 16)), vf[kk], dp);
+        }
+        const bool need_mask = (wkey_hi >= kl) || (p.causal && qlo < wkey_hi);
+        f32x16_t ds;
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][jq * 8 + g * 4]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&Dv[buf][jq * 8 + g * 4]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * jq + e;
+            float pv = fast_exp2(fmaf(s[j], c, -lv[e]));
+            if (need_mask) {
+              const int qr = qlo + jq * 8 + g * 4 + e;
+              const bool ok = key < kl && (!p.causal || key <= qr);
+              pv = ok ? pv : 0.f;
+            }
+            s[j] = pv;
+            ds[j] = pv * (dp[j] - dd[e]);
+          }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, two slices of 16)
+#pragma unroll
+        for (int kq = 0; kq < BQ / 16; ++kq) {
+          const bf16x8_t pb = pack8_bf16(s, 8 * kq);
+          const bf16x8_t db = pack8_bf16(ds, 8 * kq);
+#pragma unroll
+          for (int md = 0; md < NMD; ++md) {
+            const uint16_t* dtr = &Dt[buf][(md * 32 + l32) * TS + kq * 16 + g * 4];
+            const uint16_t* qtr = &Qt[buf][(md * 32 + l32) * TS + kq * 16 + g * 4];
+            dv[md] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint2*>(dtr),
+                                            *reinterpret_cast<const uint2*>(dtr + 8)), pb, dv[md]);
+            dk[md] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint2*>(qtr),
+                                            *reinterpret_cast<const uint2*>(qtr + 8)), db, dk[md]);
+          }
+        }
+      }
+      if (it + 1 < n_iter) swrite(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // write this lane's key row: d = 32 md + 8 (j / 4) + 4 g + (j % 4)
+  if (w * 32 + l32 < rows_here) {
+    const bool ok = key < kl;
+    uint16_t* dkr = p.dk + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+    uint16_t* dvr = p.dv + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        uint2 a, b;
+        if (ok) {
+          a.x = pack2_bf16(dk[md][4 * jj] * p.scale, dk[md][4 * jj + 1] * p.scale);
+          a.y = pack2_bf16(dk[md][4 * jj + 2] * p.scale, dk[md][4 * jj + 3] * p.scale);
+          b.x = pack2_bf16(dv[md][4 * jj], dv[md][4 * jj + 1]);
+          b.y = pack2_bf16(dv[md][4 * jj + 2], dv[md][4 * jj + 3]);
+        } else {
+          a = make_uint2(0, 0);
+          b = make_uint2(0, 0);
+        }
+        *reinterpret_cast<uint2*>(dkr + md * 32 + jj * 8) = a;
+        *reinterpret_cast<uint2*>(dvr + md * 32 + jj * 8) = b;
+      }
+  }
+}
+
+// dQ accumulator (fp32) -> bf16 dQ for every local row; padding rows 0.
+__global__ void __launch_bounds__(256) dq_finalize_kernel(const float* __restrict__ acc, const int32_t* __restrict__ rowflags,
+                                                          uint16_t* __restrict__ dq, int t_local, int hq, int d) {
+  const long long per_row = (long long)hq * d / 4;
+  const long long n = (long long)t_local * per_row;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(e / per_row);
+    uint2 pk = make_uint2(0, 0);
+    if (rowflags[t] & RF_VALID) {
+      const float4 v = *reinterpret_cast<const float4*>(acc + e * 4);
+      pk.x = pack2_bf16(v.x, v.y);
+      pk.y = pack2_bf16(v.z, v.w);
+    }
+    *reinterpret_cast<uint2*>(dq + e * 4) = pk;
+  }
+}
+
+struct TailPtrs {
+  uint16_t* p[1 + 2 * CP_ATTN_MAX_CP];
+};
+
+// Zero rows [t_local, t_alloc) of dQ and of every dK/dV part (16-byte stores).
+__global__ void __launch_bounds__(256) tail_zero_kernel(TailPtrs ptrs, int n_ptrs, long long t_local, long long t_alloc,
+                                                        int hq, int hkv, int d) {
+  const long long tail = t_alloc - t_local;
+  const long long uq = tail * hq * d / 8, ukv = tail * hkv * d / 8;
+  const long long n = uq + (long long)(n_ptrs - 1) * ukv;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
+    uint16_t* base;
+    long long u;
+    if (e < uq) {
+      base = ptrs.p[0] + t_local * hq * d;
+      u = e;
+    } else {
+      const long long r = e - uq;
+      const int which = 1 + (int)(r / ukv);
+      base = ptrs.p[which] + t_local * hkv * d;
+      u = r - (long long)(which - 1) * ukv;
+    }
+    reinterpret_cast<uint4*>(base)[u] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+static unsigned grid_for(long long n, int per_block) {
+  long long b = (n + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  return (unsigned)std::min<long long>(b, 8192);
+}
+
+}  // namespace cpattn
 
 using namespace cpattn;
 
@@ -10,5 +447,105 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
                                       const void* dout, int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
                                       int32_t causal, void* dq, void* const* dk_parts, void* const* dv_parts,
                                       void* workspace, size_t ws_bytes, void* stream) {
-  return fail(CP_ATTN_ERR_UNSUPPORTED, "backward not built yet");
+  set_error("");
+  if (!m) return fail(CP_ATTN_ERR_INVALID_ARG, "meta is NULL");
+  if (!q || !k_shards || !v_shards || !out || !lse || !dout || !dq || !dk_parts || !dv_parts)
+    return fail(CP_ATTN_ERR_INVALID_ARG, "NULL tensor argument");
+  if (causal != 1) return fail(CP_ATTN_ERR_UNSUPPORTED, "only causal attention is supported");
+  if (d != 64 && d != 128) return fail(CP_ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return fail(CP_ATTN_ERR_INVALID_ARG, "hq must be a positive multiple of hkv");
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(CP_ATTN_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  const int cp = m->cp;
+  uintptr_t al = (uintptr_t)q | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq;
+  for (int s = 0; s < cp; ++s) {
+    if (!k_shards[s] || !v_shards[s] || !dk_parts[s] || !dv_parts[s])
+      return fail(CP_ATTN_ERR_INVALID_ARG, "NULL shard / part pointer");
+    al |= (uintptr_t)k_shards[s] | (uintptr_t)v_shards[s] | (uintptr_t)dk_parts[s] | (uintptr_t)dv_parts[s];
+  }
+  if (al & 15) return fail(CP_ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  const size_t need = cp_attn_workspace_bytes(m, hq, hkv, d, 1);
+  if (!workspace || ws_bytes < need) return fail(CP_ATTN_ERR_WORKSPACE, "backward workspace missing or too small");
+  if (((uintptr_t)workspace) & 255) return fail(CP_ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != m->device)
+    return fail(CP_ATTN_ERR_INVALID_ARG, "current device differs from the metadata's device");
+  hipStream_t st = (hipStream_t)stream;
+  const int tl = m->sum.t_local;
+  cp_attn_status rc = CP_ATTN_OK;
+  if (tl > 0) {
+    const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
+    float* dq_acc = (float*)workspace;
+    float* dvec = (float*)((char*)workspace + o_al);
+    const int32_t* rowflags = m->d_tab + m->lay.rowflags;
+    hipLaunchKernelGGL(bwd_pre_kernel, dim3(grid_for((long long)tl * hq * (d / 8), 256)), dim3(256), 0, st,
+                       (const uint16_t*)dout, (const uint16_t*)out, rowflags, dvec, tl, hq, d);
+    if ((rc = hip_check(hipGetLastError(), "bwd_pre launch")) != CP_ATTN_OK) return rc;
+    BwdParams base{};
+    base.q = (const uint16_t*)q;
+    base.dout = (const uint16_t*)dout;
+    base.lse = lse;
+    base.ld_lse = m->t_alloc;
+    base.dvec = dvec;
+    base.ld_d = tl;
+    base.slot = m->d_tab + m->lay.cupl;
+    base.hq = hq;
+    base.hkv = hkv;
+    base.group = hq / hkv;
+    base.ld_q = (long long)hq * d;
+    base.ld_kv = (long long)hkv * d;
+    base.scale = softmax_scale;
+    base.c_log2 = softmax_scale * LOG2E_F;
+    base.dq_acc = dq_acc;
+    for (int i = 0; i < cp; ++i) {
+      const int s = m->sum.step_src[i];
+      StepTab tb = step_tab(m, i);
+      BwdParams p = base;
+      p.k = (const uint16_t*)k_shards[s];
+      p.v = (const uint16_t*)v_shards[s];
+      p.q_start = tb.q_start;
+      p.q_len = tb.q_len;
+      p.kv_start = tb.kv_start;
+      p.kv_len = tb.kv_len;
+      p.causal = m->sum.step_kind[i] == 0;
+      p.dk = (uint16_t*)dk_parts[s];
+      p.dv = (uint16_t*)dv_parts[s];
+      p.dq_first = (i == 0) ? 1 : 0;
+      const long long nkv = m->sum.tiles_dkdv[i] * hkv;
+      if (nkv > 0) {
+        p.items = m->d_tab + m->lay.dkdv_tiles + (int64_t)i * m->lay.dkdv_cap * 2;
+        if (d == 128)
+          hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nkv), dim3(256), 0, st, p);
+        else
+          hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nkv), dim3(256), 0, st, p);
+        if ((rc = hip_check(hipGetLastError(), "bwd_dkdv launch")) != CP_ATTN_OK) return rc;
+      }
+      const long long nq = m->sum.tiles_fwd[i] * hq;
+      if (nq > 0) {
+        p.items = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
+        if (d == 128)
+          hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(256), 0, st, p);
+        else
+          hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(256), 0, st, p);
+        if ((rc = hip_check(hipGetLastError(), "bwd_dq launch")) != CP_ATTN_OK) return rc;
+      }
+    }
+    hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for((long long)tl * hq * d / 4, 256)), dim3(256), 0, st, dq_acc,
+                       rowflags, (uint16_t*)dq, tl, hq, d);
+    if ((rc = hip_check(hipGetLastError(), "dq_finalize launch")) != CP_ATTN_OK) return rc;
+  }
+  if (m->sum.has_tail) {
+    TailPtrs tp{};
+    tp.p[0] = (uint16_t*)dq;
+    for (int s = 0; s < cp; ++s) {
+      tp.p[1 + s] = (uint16_t*)dk_parts[s];
+      tp.p[1 + cp + s] = (uint16_t*)dv_parts[s];
+    }
+    const long long tail = m->t_alloc - tl;
+    const long long n = tail * hq * d / 8 + (long long)2 * cp * tail * hkv * d / 8;
+    hipLaunchKernelGGL(tail_zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, tp, 1 + 2 * cp, (long long)tl,
+                       (long long)m->t_alloc, hq, hkv, d);
+    rc = hip_check(hipGetLastError(), "tail_zero launch");
+  }
+  return rc;
 }
