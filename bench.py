@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark: one CP rank's share of packed-THD causal ring attention, fwd+bwd.
+
+One step = the whole hot path over one batch: the per-rank metadata build,
+the forward (one flash kernel per ring step + LSE merges) and the backward
+(D preprocess, per-step dK/dV and dQ kernels, dQ finalize, tail zeroing when a
+tail exists). Inputs are seeded synthetic bf16 tensors already resident in
+HBM. The reported value is algorithmic TFLOP/s: 14 * D * Hq * causal pairs of
+the share per step (4 forward + 10 backward), divided by the measured time.
+
+Prints one JSON line. Only one GPU is used; --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+# algorithmic flops per causal pair per query head, in units of head_dim
+ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+EXEC_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_dkdv": 8, "bwd_dq": 6}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4,
+                    help="1..5: tiny / 16K pack / padded 16K pack / 131072-token GQA / 64K hierarchical pack")
+    ap.add_argument("--cpu-sample-stride", type=int, default=256,
+                    help="oracle baseline: every Nth query row of the share (0 = skip the baseline)")
+    return ap.parse_args()
+
+
+def cpu_baseline(batch, w, rank, scale, stride):
+    """The fp64 oracle, as it stands, on a bounded sample of the same share:
+    every `stride`-th local query row of the rank, all heads, forward and
+    backward (its dK/dV contributions included)."""
+    import numpy as np
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    from oracle import cp_attn_oracle as O
+    cp = w["cp"]
+    own = O.shard_rows(batch.cu, batch.cup, cp, rank)
+    valid = O.valid_mask(batch.cu, batch.cup)
+    rows = own[::stride]
+    rows = rows[valid[rows]]
+    T = batch.total_rows
+
+    def lazy(bits, sel):
+        a = np.zeros(bits.shape, dtype=np.float64)
+        a[sel] = O.bf16_to_f64(bits[sel])
+        return a
+
+    q = lazy(batch.q, rows)
+    do = lazy(batch.do, rows)
+    k = O.bf16_to_f64(batch.k)
+    v = O.bf16_to_f64(batch.v)
+    mask = np.zeros(T, dtype=bool)
+    mask[rows] = True
+    seq = np.searchsorted(batch.cup, rows, side="right") - 1
+    pairs = int(sum(int(r - batch.cup[b]) + 1 for r, b in zip(rows, seq)))
+    flops = 14 * batch.d * batch.hq * pairs
+    t0 = time.perf_counter()
+    O.attention(q, k, v, do, batch.cu, batch.cup, scale, query_mask=mask, want_grad=True)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows.size} of {own.size} local query rows (every {stride}th), all {batch.hq} heads, "
+                      f"fp64 fwd+bwd, {pairs} causal pairs, {dt:.1f} s on {threads} BLAS threads "
+                      f"({os.cpu_count()} host cpus visible)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (one rank's share played on one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from context_packed_attention_amd import api, synth
+    from context_packed_attention_amd import _lib
+
+    _lib.load()  # raises if the HIP library was not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    w = synth.workload(args.workload)
+    rank = w["ranks"][-1] if args.workload != 1 else 0
+    log(f"[bench] drawing inputs for {w['name']}")
+    t0 = time.time()
+    batch, _ = synth.make_workload(args.workload)
+    log(f"[bench] inputs drawn in {time.time() - t0:.1f} s (T={batch.total_rows})")
+    cp, hq, hkv, d = w["cp"], w["hq"], w["hkv"], w["d"]
+    scale = 1.0 / math.sqrt(d)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    cu = torch.tensor(batch.cu, dtype=torch.int32, device="cuda")
+    cup = torch.tensor(batch.cup, dtype=torch.int32, device="cuda")   # distinct, value-equal when unpadded
+    T_local = int(batch.cup[-1]) // cp
+    t_alloc = T_local
+    meta = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc)
+    gq, gk, gv, gdo = (dev_bf16(x) for x in (batch.q, batch.k, batch.v, batch.do))
+
+    def gather(src, h, s):
+        dst = torch.empty((t_alloc, h, d), dtype=torch.bfloat16, device="cuda")
+        api.cp_attn_shard_gather(meta, s, src, dst, h * d * 2)
+        return dst
+
+    q = gather(gq, hq, rank)
+    do = gather(gdo, hq, rank)
+    ks = [gather(gk, hkv, s) for s in range(cp)]
+    vs = [gather(gv, hkv, s) for s in range(cp)]
+    del gq, gk, gv, gdo
+    out = torch.empty((t_alloc, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, t_alloc), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dks = [torch.empty_like(x) for x in ks]
+    dvs = [torch.empty_like(x) for x in vs]
+    ws_f = torch.empty(api.cp_attn_workspace_bytes(meta, hq, hkv, d, 0), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(api.cp_attn_workspace_bytes(meta, hq, hkv, d, 1), dtype=torch.uint8, device="cuda")
+    step_pairs = api.step_pairs(meta)
+    pairs = sum(step_pairs)
+    flops_step = 14 * d * hq * pairs
+    stream = torch.cuda.current_stream()
+    meta.close()
+
+    # host-side cost of one metadata build on an idle device (it ends in the
+    # library's single synchronisation)
+    torch.cuda.synchronize()
+    meta_ms = []
+    for _ in range(5):
+        t = time.perf_counter()
+        m = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+        meta_ms.append((time.perf_counter() - t) * 1e3)
+        m.close()
+
+    def one_step():
+        m = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+        api.cp_attn_fwd(m, q, ks, vs, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream)
+        api.cp_attn_bwd(m, q, ks, vs, out, lse, do, hq, hkv, d, scale, 1, dq, dks, dvs, ws_b, stream=stream)
+        return m
+
+    log(f"[bench] warmup {args.warmup}")
+    held = []
+    for _ in range(args.warmup):
+        held.append(one_step())
+    torch.cuda.synchronize()
+    for m in held:
+        m.close()
+    held.clear()
+    log(f"[bench] timing {args.steps} steps")
+    api.cp_attn_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        held.append(one_step())
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    api.cp_attn_timing_enable(False)
+    per_kernel = api.cp_attn_timing_read()
+    for m in held:
+        m.close()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    kernels = {}
+    for name, (ms, n) in per_kernel.items():
+        entry = {"launches_per_step": n / args.steps, "ms_per_step": ms / args.steps, "avg_launch_ms": ms / n}
+        if name in ALGO_FLOPS_PER_PAIR:
+            fl = ALGO_FLOPS_PER_PAIR[name] * d * hq * pairs * args.steps
+            entry["algo_tflops"] = fl / (ms * 1e-3) / 1e12
+            entry["exec_tflops"] = EXEC_FLOPS_PER_PAIR[name] * d * hq * pairs * args.steps / (ms * 1e-3) / 1e12
+        kernels[name] = entry
+    dom = max(per_kernel.items(), key=lambda kv: kv[1][0])[0]
+    dom_ms, dom_n = per_kernel[dom]
+    if dom in ALGO_FLOPS_PER_PAIR:
+        per_launch = ALGO_FLOPS_PER_PAIR[dom] * d * hq * pairs * args.steps / dom_n
+        achieved = per_launch / (dom_ms / dom_n * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algo_flops_per_launch": per_launch, "avg_launch_ms": dom_ms / dom_n}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": None, "traffic": None}
+
+    cpu = None
+    if args.cpu_sample_stride > 0:
+        log("[bench] oracle CPU baseline")
+        cpu = cpu_baseline(batch, w, rank, scale, args.cpu_sample_stride)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s ({cpu['seconds']:.1f} s)")
+
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s per CP-rank share (1 MI355X), % of bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO)",
+        "config": {"workload": w["name"], "cp_size": cp, "cp_rank": rank, "tokens": batch.total_rows,
+                   "t_local": T_local, "hq": hq, "hkv": hkv, "head_dim": d, "causal": True,
+                   "pairs": pairs, "step_pairs": step_pairs, "flops_per_step": flops_step,
+                   "parallelism": "one CP rank's share, all ring steps on one GPU"},
+        "metadata_call_ms": round(sorted(meta_ms)[len(meta_ms) // 2], 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

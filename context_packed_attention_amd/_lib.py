@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "HINT_MISMATCH",
 EXPORTED = [
     "cp_attn_rank_metadata", "cp_attn_meta_summary", "cp_attn_meta_export", "cp_attn_meta_free",
     "cp_attn_workspace_bytes", "cp_attn_fwd", "cp_attn_bwd", "cp_attn_shard_gather", "cp_attn_last_error",
+    "cp_attn_timing_enable", "cp_attn_timing_read",
 ]
 
 
@@ -67,6 +68,10 @@ def load(path: str | None = None) -> C.CDLL:
     lib.cp_attn_bwd.restype = st
     lib.cp_attn_shard_gather.argtypes = [vp, i32, vp, vp, C.c_size_t, vp]
     lib.cp_attn_shard_gather.restype = st
+    lib.cp_attn_timing_enable.argtypes = [i32]
+    lib.cp_attn_timing_enable.restype = st
+    lib.cp_attn_timing_read.argtypes = [C.c_char_p, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64), i32]
+    lib.cp_attn_timing_read.restype = i32
     lib.cp_attn_last_error.argtypes = []
     lib.cp_attn_last_error.restype = C.c_char_p
     _lib = lib

@@ -151,3 +151,64 @@ def cp_attn_shard_gather(meta: Meta, shard: int, global_rows, local_rows, row_by
 
 def cp_attn_last_error() -> str:
     return L.load().cp_attn_last_error().decode(errors="replace")
+
+
+def cp_attn_timing_enable(on: bool):
+    _check(L.load().cp_attn_timing_enable(1 if on else 0), "cp_attn_timing_enable")
+
+
+def cp_attn_timing_read(max_kernels: int = 32) -> dict:
+    """{kernel name: (total ms, launches)} of the launches recorded since enabling."""
+    name_len = 64
+    names = C.create_string_buffer(max_kernels * name_len)
+    ms = (C.c_double * max_kernels)()
+    cnt = (C.c_int64 * max_kernels)()
+    n = L.load().cp_attn_timing_read(names, name_len, ms, cnt, max_kernels)
+    if n < 0:
+        raise CpAttnError(L.ERR_HIP, "cp_attn_timing_read", "event synchronisation failed")
+    raw = names.raw
+    out = {}
+    for i in range(n):
+        nm = raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (float(ms[i]), int(cnt[i]))
+    return out
+
+
+def meta_tables(meta: Meta) -> dict:
+    """The exported integer tables as named lists (layout of cp_attn_meta_export)."""
+    a = [int(x) for x in cp_attn_meta_export(meta)]
+    B, cp, rank, pad, tl, tail, nst = a[:7]
+    o = 8
+    out = {"B": B, "cp": cp, "rank": rank, "pad_between_seqs": pad, "t_local": tl, "has_tail": tail}
+
+    def take(n):
+        nonlocal o
+        v = a[o:o + n]
+        o += n
+        return v
+
+    out["chunk"] = take(B)
+    out["cu_padded_local"] = take(B + 1)
+    out["cu_padded_half"] = take(B + 1)
+    for s in range(cp):
+        for k in ("full", "first", "second"):
+            out[f"cu_{k}_{s}"] = take(B + 1)
+    out["steps"] = []
+    for _ in range(nst):
+        kind, src = take(2)
+        out["steps"].append({"kind": kind, "src": src, "q_start": take(B), "q_len": take(B),
+                             "kv_start": take(B), "kv_len": take(B)})
+    return out
+
+
+def step_pairs(meta: Meta) -> list[int]:
+    """Causal (query, key) pairs each ring step computes, diagonal included:
+    n(n+1)/2 per sequence at the causal step, q_len * kv_len otherwise."""
+    t = meta_tables(meta)
+    pairs = []
+    for st in t["steps"]:
+        if st["kind"] == 0:
+            pairs.append(sum(n * (n + 1) // 2 for n in st["q_len"]))
+        else:
+            pairs.append(sum(a * b for a, b in zip(st["q_len"], st["kv_len"])))
+    return pairs

@@ -478,8 +478,10 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     float* dq_acc = (float*)workspace;
     float* dvec = (float*)((char*)workspace + o_al);
     const int32_t* rowflags = m->d_tab + m->lay.rowflags;
+    timing_begin(st, "bwd_pre");
     hipLaunchKernelGGL(bwd_pre_kernel, dim3(grid_for((long long)tl * hq * (d / 8), 256)), dim3(256), 0, st,
                        (const uint16_t*)dout, (const uint16_t*)out, rowflags, dvec, tl, hq, d);
+    timing_end(st);
     if ((rc = hip_check(hipGetLastError(), "bwd_pre launch")) != CP_ATTN_OK) return rc;
     BwdParams base{};
     base.q = (const uint16_t*)q;
@@ -514,24 +516,30 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
       const long long nkv = m->sum.tiles_dkdv[i] * hkv;
       if (nkv > 0) {
         p.items = m->d_tab + m->lay.dkdv_tiles + (int64_t)i * m->lay.dkdv_cap * 2;
+        timing_begin(st, "bwd_dkdv");
         if (d == 128)
           hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nkv), dim3(256), 0, st, p);
         else
           hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nkv), dim3(256), 0, st, p);
+        timing_end(st);
         if ((rc = hip_check(hipGetLastError(), "bwd_dkdv launch")) != CP_ATTN_OK) return rc;
       }
       const long long nq = m->sum.tiles_fwd[i] * hq;
       if (nq > 0) {
         p.items = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
+        timing_begin(st, "bwd_dq");
         if (d == 128)
           hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(256), 0, st, p);
         else
           hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(256), 0, st, p);
+        timing_end(st);
         if ((rc = hip_check(hipGetLastError(), "bwd_dq launch")) != CP_ATTN_OK) return rc;
       }
     }
+    timing_begin(st, "dq_finalize");
     hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for((long long)tl * hq * d / 4, 256)), dim3(256), 0, st, dq_acc,
                        rowflags, (uint16_t*)dq, tl, hq, d);
+    timing_end(st);
     if ((rc = hip_check(hipGetLastError(), "dq_finalize launch")) != CP_ATTN_OK) return rc;
   }
   if (m->sum.has_tail) {
@@ -543,8 +551,10 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     }
     const long long tail = m->t_alloc - tl;
     const long long n = tail * hq * d / 8 + (long long)2 * cp * tail * hkv * d / 8;
+    timing_begin(st, "tail_zero");
     hipLaunchKernelGGL(tail_zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, tp, 1 + 2 * cp, (long long)tl,
                        (long long)m->t_alloc, hq, hkv, d);
+    timing_end(st);
     rc = hip_check(hipGetLastError(), "tail_zero launch");
   }
   return rc;

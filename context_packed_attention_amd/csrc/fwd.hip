@@ -298,10 +298,12 @@ static cp_attn_status launch_fwd_step(const cp_attn_meta* m, int i, const FwdPar
   const long long blocks = (long long)tiles * p.hq;
   if (blocks == 0) return CP_ATTN_OK;
   if (blocks > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
+  timing_begin(st, "fwd_step");
   if (d == 128)
     hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  timing_end(st);
   return hip_check(hipGetLastError(), "fwd_step launch");
 }
 
@@ -390,16 +392,20 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
     rc = launch_fwd_step(m, i, p, d, (int)m->sum.tiles_fwd[i], st);
     if (rc != CP_ATTN_OK) return rc;
     if (i >= 1) {
+      timing_begin(st, "lse_merge");
       hipLaunchKernelGGL(lse_merge_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, acc_o, acc_l, part_o,
                          part_l, rowflags, m->sum.step_kind[i], (i == m->cp - 1) ? 1 : 0, (uint16_t*)out, lse, tl, hq,
                          d, (long long)m->t_alloc);
+      timing_end(st);
       rc = hip_check(hipGetLastError(), "lse_merge launch");
       if (rc != CP_ATTN_OK) return rc;
     }
   }
   if (m->cp == 1) {
+    timing_begin(st, "lse_merge");
     hipLaunchKernelGGL(lse_merge_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, acc_o, acc_l, part_o, part_l,
                        rowflags, -1, 1, (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
+    timing_end(st);
     rc = hip_check(hipGetLastError(), "lse_merge launch");
   }
   return rc;

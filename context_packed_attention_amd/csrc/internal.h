@@ -77,6 +77,10 @@ struct cp_attn_meta {
 
 namespace cpattn {
 
+// per-kernel event timing (no-ops unless enabled through the C ABI)
+void timing_begin(hipStream_t st, const char* name);
+void timing_end(hipStream_t st);
+
 // thread-local error message
 void set_error(const std::string& msg);
 cp_attn_status fail(cp_attn_status st, const std::string& msg);

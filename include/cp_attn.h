@@ -194,6 +194,24 @@ cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, const void* con
 cp_attn_status cp_attn_shard_gather(const cp_attn_meta* m, int32_t shard, const void* global,
                                     void* local, size_t row_bytes, void* stream);
 
+/*
+ * Kernel timing (measurement tooling, not on the numerical path). While
+ * enabled, every kernel launched by cp_attn_fwd / cp_attn_bwd is bracketed by
+ * a pair of HIP events recorded on its launch stream (so the timing includes
+ * nothing but that stream's work between the two records). Do not enable it
+ * while capturing a HIP graph. Not thread-safe; meant for one benchmarking
+ * thread.
+ * cp_attn_timing_enable(1) clears earlier records and starts recording;
+ * cp_attn_timing_enable(0) stops recording.
+ * cp_attn_timing_read waits for the recorded events and fills up to `max`
+ * entries: names (each in a `name_len`-byte slot of `names`, host buffer of
+ * max * name_len bytes, NUL-terminated), the summed duration in milliseconds
+ * and the launch count per kernel; returns the number of distinct kernels
+ * (or -1 on a HIP error) and clears the records.
+ */
+cp_attn_status cp_attn_timing_enable(int32_t on);
+int32_t cp_attn_timing_read(char* names, int32_t name_len, double* total_ms, int64_t* launches, int32_t max);
+
 /* Thread-local description of the last failure ("" if none). */
 const char* cp_attn_last_error(void);
 
