@@ -70,23 +70,22 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
   }
 }
 
-// dQ of one ring step. Block = 4 wavefronts x 32 query rows of one head; key
-// tiles of 32 rows are staged in LDS three ways (K and V row-major for the
-// transposed scores S^T = K Q^T and dP^T = V dO^T, and K^T for dQ^T = K^T dS^T),
-// double-buffered: half the threads fetch K, the other half V.
+// dQ of one ring step. Block = 4 wavefronts x 32 query rows of one head;
+// key tiles of 64 rows: K and V are copied straight into padded LDS tiles
+// (double-buffered). Row-major reads of K and V feed the transposed scores
+// S^T = K Q^T and dP^T = V dO^T (lane = one query row); transposing reads of
+// the same K tile feed dQ^T = K^T dS^T. Keys past the step's key range read as
+// zeros, so their K^T rows contribute nothing and need no mask.
 template <int D>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
-  constexpr int BM = FWD_BM, BN = 32;
-  constexpr int KS = D + 8, TS = BN + 4;
+  constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
-  constexpr int NB = (BN / 4) * (D / 8);  // 4x8 blocks per tile and tensor
-  static_assert(NB <= 128, "K blocks on threads [0,128), V blocks on [128,256)");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TS];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, BN>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, BN>() / 2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   int item, head;
   map_block(blockIdx.x, p.hq, item, head);
   const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
@@ -116,75 +115,56 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int md = 0; md < NMD; ++md) acc[md] = zero16();
 
-  const bool is_k = tid < NB, is_v = tid >= 128 && tid < 128 + NB;
-  const int blk = is_k ? tid : tid - 128;
-  const int kg = blk / (D / 8), dc = blk % (D / 8);
-  const uint16_t* src = (is_k ? p.k : p.v) + (long long)kvs * p.ld_kv + kvh * D + dc * 8;
-  uint4 rg[4];
-
-  auto gload = [&](int kt) {
-    if (is_k || is_v) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * BN + 4 * kg + r;
-        rg[r] = key < kl ? *reinterpret_cast<const uint4*>(src + (long long)key * p.ld_kv) : make_uint4(0, 0, 0, 0);
-      }
-    }
+  const int ldb = (int)(p.ld_kv * 2);
+  const long long range_bytes = (long long)kl * ldb;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
+  auto issue = [&](int kt, int buf) {
+    load_tile_lds<D, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
   };
-  auto swrite = [&](int buf) {
-    if (is_k || is_v) {
-      uint16_t* rm = is_k ? Ks[buf] : Vs[buf];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&rm[(4 * kg + r) * KS + dc * 8]) = rg[r];
-      if (is_k) store_transposed_4x8(&Kt[buf][(dc * 8) * TS + 4 * kg], TS, rg[0], rg[1], rg[2], rg[3]);
-    }
-  };
+  if (nt > 0) issue(0, 0);
 
-  if (nt > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nt) gload(kt + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
     const int k0 = kt * BN;
     const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
     if (active) {
-      f32x16_t s = zero16(), dp = zero16();
-      const uint16_t* krow = &Ks[buf][l32 * KS + g * 8];
-      const uint16_t* vrow = &Vs[buf][l32 * KS + g * 8];
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = zero16();
+        dp[mb] = zero16();
+      }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(krow + kk * 16)), qf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + kk * 16)), df[kk], dp);
-      }
-      const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float pv = fast_exp2(fmaf(s[j], c, -lse2));
-        if (need_mask) {
-          const int key = k0 + (j >> 2) * 8 + g * 4 + (j & 3);
-          const bool ok = key < kl && (!p.causal || key <= qrow);
-          pv = ok ? pv : 0.f;
+        for (int mb = 0; mb < 2; ++mb) {
+          s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
+          dp[mb] = mfma32x32x16(lds_read_row<D>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
         }
-        s[j] = pv * (dp[j] - dq_d);  // dS^T
       }
+      const bool need_mask = p.causal && k0 + BN - 1 > wrow_lo;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float pv = fast_exp2(fmaf(s[mb][j], c, -lse2));
+          if (need_mask) pv = (k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3) <= qrow) ? pv : 0.f;
+          s[mb][j] = pv * (dp[mb][j] - dq_d);  // dS^T
+        }
 #pragma unroll
       for (int kk2 = 0; kk2 < BN / 16; ++kk2) {
-        const bf16x8_t ds = pack8_bf16(s, 8 * kk2);
+        const bf16x8_t ds = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
-        for (int md = 0; md < NMD; ++md) {
-          const uint16_t* tr = &Kt[buf][(md * 32 + l32) * TS + kk2 * 16 + g * 4];
-          const uint2 lo = *reinterpret_cast<const uint2*>(tr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(tr + 8);
-          acc[md] = mfma32x32x16(as_bf16x8(lo, hi), ds, acc[md]);
-        }
+        for (int md = 0; md < NMD; ++md)
+          acc[md] = mfma32x32x16(lds_read_tr<D>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
       }
     }
-    if (kt + 1 < nt) swrite(buf ^ 1);
-    __syncthreads();
   }
   if (qok) {
     float* dst = p.dq_acc + (long long)(qs + qrow) * p.hq * D + head * D + g * 4;
@@ -208,28 +188,28 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 }
 
 // dK/dV of one ring step for the source shard's key rows. Block = 4
-// wavefronts x 32 key rows of one KV head (DKDV_BN = 128 keys); loops over the
-// query heads of the group and the step's query rows in tiles of 32. Q and dO
-// tiles are staged in LDS row-major (scores S = Q K^T, dP = dO V^T) and
-// transposed (dK^T = Q^T dS, dV^T = dO^T P), double-buffered.
-// Rows of the part outside the step's key range are written as zeros, so the
-// whole shard-s part is defined after the step.
+// wavefronts x 32 key rows of one KV head (DKDV_BN = 128 keys), K in
+// registers and V in LDS; loops over the query heads of the group and the step's query rows
+// in tiles of 32. Q and dO tiles are copied straight into padded LDS tiles
+// (double-buffered) together with the rows' LSE and D. Row-major reads feed
+// S = Q K^T and dP = dO V^T (lane = one key column); transposing reads feed
+// dV^T += dO^T P and dK^T += Q^T dS (lane = one key row of the output).
+// Query rows past the step's range read as zeros (Q = dO = D = 0), which
+// makes their dS and P.dO contributions vanish; key rows past the key range
+// are computed but written as zeros. Rows of the part outside the step's key
+// range are written as zeros too, so the whole shard-s part is defined.
 template <int D>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = DKDV_BN, BQ = 32;
-  constexpr int QS = D + 8, TS = BQ + 4;
   constexpr int NKK = D / 16, NMD = D / 32;
-  constexpr int NB = (BQ / 4) * (D / 8);  // 4x8 blocks per q tile and tensor
-  static_assert(2 * NB <= 256, "one block per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BQ * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TS];
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Dv[2][BQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][tile_bytes<D, BQ>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][tile_bytes<D, BQ>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vt[tile_bytes<D, BK>() / 2];  // the block's V rows
+  __shared__ __attribute__((aligned(16))) float LD[2][2 * BQ];  // per buffer: LSE rows, then D rows
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   int item, kvh;
   map_block(blockIdx.x, p.hkv, item, kvh);
   const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
@@ -255,113 +235,94 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   const int n_iter = n_qt * p.group;
 
   if (n_iter > 0) {
-    bf16x8_t kf[NKK], vf[NKK];
+    // K rows of this lane's key in registers, the block's V rows in LDS
+    bf16x8_t kf[NKK];
     {
       const bool ok = key < kl;
       const long long off = (long long)(kvs + (ok ? key : 0)) * p.ld_kv + kvh * D + g * 8;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+      for (int kk = 0; kk < NKK; ++kk)
         kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.k + off + kk * 16) : make_uint4(0, 0, 0, 0));
-        vf[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.v + off + kk * 16) : make_uint4(0, 0, 0, 0));
-      }
+      const int ldkv = (int)(p.ld_kv * 2);
+      const __amdgpu_buffer_rsrc_t vrs =
+          make_rsrc(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, (long long)nk * ldkv);
+      load_tile_lds<D, BK>(vrs, Vt, 0, ldkv, w, lane);
     }
-    uint4 rg[4];
-    float lval = 0.f;
-    const bool is_q = tid < NB, is_d = tid >= 128 && tid < 128 + NB;
-    const int blk = is_q ? tid : tid - 128;
-    const int qg = blk / (D / 8), dc = blk % (D / 8);
-
-    auto gload = [&](int it) {
-      const int hh = kvh * p.group + it / n_qt;
-      const int qt = qt_begin + it % n_qt;
-      if (is_q || is_d) {
-        const uint16_t* src = is_q ? p.q : p.dout;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qrow = qt * BQ + 4 * qg + r;
-          rg[r] = qrow < ql ? *reinterpret_cast<const uint4*>(src + (long long)(qs + qrow) * p.ld_q + hh * D + dc * 8)
-                            : make_uint4(0, 0, 0, 0);
-        }
-      }
-      if (tid >= 64 && tid < 64 + BQ) {
-        const int qrow = qt * BQ + tid - 64;
-        lval = qrow < ql ? p.lse[(long long)hh * p.ld_lse + qs + qrow] * LOG2E_F : __builtin_huge_valf();
-      } else if (tid >= 192 && tid < 192 + BQ) {
-        const int qrow = qt * BQ + tid - 192;
-        lval = qrow < ql ? p.dvec[(long long)hh * p.ld_d + qs + qrow] : 0.f;
+    const int ldb = (int)(p.ld_q * 2);
+    const long long range = (long long)ql * ldb;
+    // per query head of the group: resources over the step's query rows
+    auto issue = [&](int hh, int qt, int buf) {
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + (long long)qs * p.ld_q + hh * D, range);
+      const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + (long long)qs * p.ld_q + hh * D, range);
+      const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse + (long long)hh * p.ld_lse + qs, (long long)ql * 4);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.dvec + (long long)hh * p.ld_d + qs, (long long)ql * 4);
+      load_tile_lds<D, BQ>(qr, Qs[buf], qt * BQ * ldb, ldb, w, lane);
+      load_tile_lds<D, BQ>(dr, Ds[buf], qt * BQ * ldb, ldb, w, lane);
+      if (w == 0) {
+        // lane l writes LDS bytes [16 l, 16 l + 16) of LD[buf]: lanes 0..7 the
+        // tile's LSE rows, lanes 8..15 its D rows (4 rows per lane)
+        if (lane < BQ / 4)
+          load_lds16(lr, &LD[buf][0], qt * BQ * 4 + lane * 16);
+        else if (lane < BQ / 2)
+          load_lds16(vr, &LD[buf][0], qt * BQ * 4 + (lane - BQ / 4) * 16);
       }
     };
-    auto swrite = [&](int buf) {
-      if (is_q || is_d) {
-        uint16_t* rm = is_q ? Qs[buf] : Ds[buf];
-        uint16_t* tm = is_q ? Qt[buf] : Dt[buf];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&rm[(4 * qg + r) * QS + dc * 8]) = rg[r];
-        store_transposed_4x8(&tm[(dc * 8) * TS + 4 * qg], TS, rg[0], rg[1], rg[2], rg[3]);
-      }
-      if (tid >= 64 && tid < 64 + BQ) Ls[buf][tid - 64] = lval;
-      else if (tid >= 192 && tid < 192 + BQ) Dv[buf][tid - 192] = lval;
-    };
+    static_assert(sizeof(LD[0]) == 2 * BQ * 4, "LSE/D layout");
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
-    const int wkey_lo = k0 + w * 32, wkey_hi = wkey_lo + 31;
+    int hh = kvh * p.group, qt = qt_begin;
+    issue(hh, qt, 0);
+    const int wkey_hi = k0 + w * 32 + 31;
     for (int it = 0; it < n_iter; ++it) {
       const int buf = it & 1;
-      if (it + 1 < n_iter) gload(it + 1);
-      const int qt = qt_begin + it % n_qt;
-      const int qlo = qt * BQ, qhi = qlo + BQ - 1;
-      const bool active = wkey_lo < kl && !(p.causal && qhi < wkey_lo);
-      if (active) {
+      const int cur_qt = qt;
+      if (++qt == qt_end) {
+        qt = qt_begin;
+        ++hh;
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (it + 1 < n_iter) issue(hh, qt, buf ^ 1);
+      // every wavefront computes every tile (no branch around the MFMAs, so
+      // the accumulators stay in place across iterations); tiles wholly in
+      // the future of a wavefront's keys are zeroed by the causal mask
+      const int qlo = cur_qt * BQ;
+      {
         // S = Q K^T and dP = dO V^T: rows q (this lane: 16 of them), column key
         f32x16_t s = zero16(), dp = zero16();
-        const uint16_t* qrow_p = &Qs[buf][l32 * QS + g * 8];
-        const uint16_t* drow_p = &Ds[buf][l32 * QS + g * 8];
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(qrow_p + kk * 16)), kf[kk], s);
-          dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(drow_p + kk * 16)), vf[kk], dp);
+          s = mfma32x32x16(lds_read_row<D>(Qs[buf], l32, 2 * kk + g), kf[kk], s);
+          dp = mfma32x32x16(lds_read_row<D>(Ds[buf], l32, 2 * kk + g),
+                            lds_read_row<D>(Vt, w * 32 + l32, 2 * kk + g), dp);
         }
-        const bool need_mask = (wkey_hi >= kl) || (p.causal && qlo < wkey_hi);
-        f32x16_t ds;
+        const bool need_mask = p.causal && qlo < wkey_hi;
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][jq * 8 + g * 4]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&Dv[buf][jq * 8 + g * 4]);
+          const float4 l4 = *reinterpret_cast<const float4*>(&LD[buf][jq * 8 + g * 4]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&LD[buf][BQ + jq * 8 + g * 4]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * jq + e;
-            float pv = fast_exp2(fmaf(s[j], c, -lv[e]));
-            if (need_mask) {
-              const int qr = qlo + jq * 8 + g * 4 + e;
-              const bool ok = key < kl && (!p.causal || key <= qr);
-              pv = ok ? pv : 0.f;
-            }
-            s[j] = pv;
-            ds[j] = pv * (dp[j] - dd[e]);
+            float pv = fast_exp2(fmaf(s[j], c, -lv[e] * LOG2E_F));
+            if (need_mask) pv = (key <= qlo + jq * 8 + g * 4 + e) ? pv : 0.f;
+            s[j] = pv;                     // P
+            dp[j] = pv * (dp[j] - dd[e]);  // dS, in place
           }
         }
         // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, two slices of 16)
 #pragma unroll
         for (int kq = 0; kq < BQ / 16; ++kq) {
           const bf16x8_t pb = pack8_bf16(s, 8 * kq);
-          const bf16x8_t db = pack8_bf16(ds, 8 * kq);
+          const bf16x8_t db = pack8_bf16(dp, 8 * kq);
 #pragma unroll
           for (int md = 0; md < NMD; ++md) {
-            const uint16_t* dtr = &Dt[buf][(md * 32 + l32) * TS + kq * 16 + g * 4];
-            const uint16_t* qtr = &Qt[buf][(md * 32 + l32) * TS + kq * 16 + g * 4];
-            dv[md] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint2*>(dtr),
-                                            *reinterpret_cast<const uint2*>(dtr + 8)), pb, dv[md]);
-            dk[md] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint2*>(qtr),
-                                            *reinterpret_cast<const uint2*>(qtr + 8)), db, dk[md]);
+            dv[md] = mfma32x32x16(lds_read_tr<D>(Ds[buf], kq * 16, md * 32, lane), pb, dv[md]);
+            dk[md] = mfma32x32x16(lds_read_tr<D>(Qs[buf], kq * 16, md * 32, lane), db, dk[md]);
           }
         }
       }
-      if (it + 1 < n_iter) swrite(buf ^ 1);
-      __syncthreads();
     }
   }
   // write this lane's key row: d = 32 md + 8 (j / 4) + 4 g + (j % 4)
@@ -470,6 +431,8 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != m->device)
     return fail(CP_ATTN_ERR_INVALID_ARG, "current device differs from the metadata's device");
+  if ((long long)m->t_alloc * hq * d * 2 >= (1ll << 31))
+    return fail(CP_ATTN_ERR_UNSUPPORTED, "local tensors must stay below 2 GiB (32-bit buffer offsets)");
   hipStream_t st = (hipStream_t)stream;
   const int tl = m->sum.t_local;
   cp_attn_status rc = CP_ATTN_OK;

@@ -38,27 +38,27 @@ struct FwdParams {
 };
 
 // One block = 4 wavefronts = 128 query rows of one head; each wavefront owns
-// 32 query rows. Key/value tiles of 64 rows are staged in LDS (K row-major,
-// V transposed) with a register-prefetched double buffer. Scores are computed
-// transposed (S^T = K Q^T) so each lane owns one query row: the online
-// softmax needs one cross-lane max per tile, and the output O^T = V^T P^T
-// keeps per-lane row scaling. Rescaling is lazy: the running max only moves
-// when a tile's max exceeds it by more than 2^8 in exp2 units.
+// 32 query rows. K and V tiles of 64 rows are copied straight from global
+// memory into padded LDS tiles (buffer loads with the lds modifier, no
+// register staging), double-buffered. Scores are computed transposed
+// (S^T = K Q^T, K rows as the A operand) so each lane owns one query row: the
+// online softmax needs one cross-lane max per tile, and O^T = V^T P^T takes
+// V^T through transposing LDS reads and keeps per-lane row scaling. Keys past
+// the step's key range read as zeros (buffer range check) and are masked.
+// Rescaling is lazy: the running max only moves when a tile's max exceeds it
+// by more than 2^8 in exp2 units.
 template <int D>
 __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
   constexpr int BM = FWD_BM, BN = 64;
-  constexpr int KS = D + 8;   // K tile row stride (bf16)
-  constexpr int VS = BN + 4;  // V^T tile row stride (bf16)
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
-  constexpr int KCH = BN * D / 8 / 256;      // 16-byte K chunks per thread
-  constexpr int VBLK = (BN / 4) * (D / 8);   // 4x8 V blocks per tile
   static_assert(BM == 128, "4 wavefronts x 32 rows");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, BN>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, BN>() / 2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   int item, head;
   map_block(blockIdx.x, p.hq, item, head);
   const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
@@ -87,64 +87,35 @@ __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
   for (int md = 0; md < NMD; ++md) o[md] = zero16();
   float m_run = NEG_INF_F, l_run = 0.f;
 
-  const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
-  const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
-  uint4 kreg[KCH];
-  uint4 vreg[4];
-  const int vkg = tid / (D / 8), vdc = tid % (D / 8);
-
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int ch = 0; ch < KCH; ++ch) {
-      const int id = tid + 256 * ch;
-      const int row = id / (D / 8), col = id % (D / 8);
-      const int key = kt * BN + row;
-      kreg[ch] = key < kl ? *reinterpret_cast<const uint4*>(kbase + (long long)key * p.ld_kv + col * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < VBLK) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * BN + 4 * vkg + r;
-        vreg[r] = key < kl ? *reinterpret_cast<const uint4*>(vbase + (long long)key * p.ld_kv + vdc * 8)
-                           : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int ch = 0; ch < KCH; ++ch) {
-      const int id = tid + 256 * ch;
-      const int row = id / (D / 8), col = id % (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[buf][row * KS + col * 8]) = kreg[ch];
-    }
-    if (tid < VBLK) store_transposed_4x8(&Vt[buf][(vdc * 8) * VS + 4 * vkg], VS, vreg[0], vreg[1], vreg[2], vreg[3]);
+  const int ldb = (int)(p.ld_kv * 2);
+  const long long range_bytes = (long long)kl * ldb;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
+  auto issue = [&](int kt, int buf) {
+    load_tile_lds<D, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
   };
 
-  if (nt > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
+  if (nt > 0) issue(0, 0);
 
   const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nt) gload(kt + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
     const int k0 = kt * BN;
     const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
     if (active) {
       f32x16_t s[2];
+      s[0] = zero16();
+      s[1] = zero16();
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = zero16();
-        const uint16_t* kr = &Ks[buf][(mb * 32 + l32) * KS + g * 8];
+      for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(kr + kk * 16));
-          s[mb] = mfma32x32x16(a, qf[kk], s[mb]);
-        }
+        for (int mb = 0; mb < 2; ++mb)
+          s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
       }
       const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
       if (need_mask) {
@@ -188,16 +159,10 @@ __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
       for (int kk2 = 0; kk2 < 4; ++kk2) {
         const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
-        for (int md = 0; md < NMD; ++md) {
-          const uint16_t* vr = &Vt[buf][(md * 32 + l32) * VS + kk2 * 16 + g * 4];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          o[md] = mfma32x32x16(as_bf16x8(lo, hi), pb, o[md]);
-        }
+        for (int md = 0; md < NMD; ++md)
+          o[md] = mfma32x32x16(lds_read_tr<D>(Vs[buf], kk2 * 16, md * 32, lane), pb, o[md]);
       }
     }
-    if (kt + 1 < nt) swrite(buf ^ 1);
-    __syncthreads();
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
@@ -361,6 +326,8 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   if (((uintptr_t)workspace) & 255) return fail(CP_ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const int tl = m->sum.t_local;
   if (tl == 0) return CP_ATTN_OK;
+  if ((long long)m->t_alloc * hkv * d * 2 >= (1ll << 31))
+    return fail(CP_ATTN_ERR_UNSUPPORTED, "a K/V shard must stay below 2 GiB (32-bit buffer offsets)");
   hipStream_t st = (hipStream_t)stream;
   const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
   const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);

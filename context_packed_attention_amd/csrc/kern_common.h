@@ -104,4 +104,84 @@ __device__ __forceinline__ void map_block(int bid, int nheads, int& item, int& h
   }
 }
 
+// ---------------------------------------------------------------- LDS tiles
+// Row-major tiles (rows x D bf16) live in LDS with padded rows: 304 bytes per
+// row for D = 128 (19 units of 16 bytes, 16 used) and 144 bytes for D = 64
+// (9 units, 8 used). On gfx950's 64-bank LDS (16 lanes served per cycle for
+// b128 and b64 reads) these strides keep both access patterns conflict-free
+// while every address stays linear in the unrolled loop indices:
+//  * b128 operand reads, where 16 lanes read one unit of 16 consecutive rows;
+//  * ds_read_b64_tr_b16 transposed reads, where a 16-lane group reads 4
+//    consecutive rows (first row a multiple of 4) x 32 consecutive bytes.
+template <int D>
+__host__ __device__ constexpr int tile_rowb() { return D == 128 ? 304 : 144; }
+template <int D, int ROWS>
+__host__ __device__ constexpr int tile_bytes() { return ROWS * tile_rowb<D>(); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// Direct global->LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l of the wavefront writes LDS bytes [chunk + 16 l, chunk + 16 l + 16).
+// Offsets at or past the resource's num_records read as zeros.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds_chunk, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_chunk, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr int OOB_OFFSET = 0x7ffffff0;  // any offset past num_records reads zeros
+
+// Copy one tile of ROWS x D bf16 (global rows `ld_bytes` apart, starting at
+// byte `row0_off` of the resource) into a padded LDS tile. The tile is filled
+// as a linear run of 16-byte units in 1 KB chunks shared by the block's 4
+// wavefronts; a lane whose unit is row padding loads zeros, lanes past the
+// tile's end stay idle.
+template <int D, int ROWS>
+__device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, int row0_off,
+                                              int ld_bytes, int wave, int lane) {
+  constexpr int SU = tile_rowb<D>() / 16;   // units per padded row
+  constexpr int UPR = D * 2 / 16;           // units per data row
+  constexpr int UNITS = ROWS * SU;
+  constexpr int CHUNKS = (UNITS + 63) / 64;
+#pragma unroll
+  for (int cc = 0; cc < (CHUNKS + 3) / 4; ++cc) {
+    const int c = cc * 4 + wave;
+    const int u = c * 64 + lane;
+    if ((CHUNKS % 4 == 0 || c < CHUNKS) && (UNITS % 64 == 0 || u < UNITS)) {
+      const int row = u / SU, unit = u % SU;
+      const int off = unit < UPR ? row0_off + row * ld_bytes + unit * 16 : OOB_OFFSET;
+      load_lds16(rsrc, reinterpret_cast<char*>(lds_tile) + c * 1024, off);
+    }
+  }
+}
+
+// b128 read of 16-byte unit `unit` of `row`.
+template <int D>
+__device__ __forceinline__ bf16x8_t lds_read_row(const uint16_t* tile, int row, int unit) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + row * tile_rowb<D>() + unit * 16));
+}
+
+// Transposed operand (ds_read_b64_tr_b16) for the 32-wide MFMA A operand
+// with k running over tile rows: lane (32 g + i) receives column col0 + i of
+// rows k0 + 4 g + {0..3} and k0 + 8 + 4 g + {0..3} (col0 a multiple of 32, k0
+// a multiple of 16). Within each 16-lane group, lane j supplies the address
+// of row (first + j / 4), columns 4 (j % 4) .. +3 of its 16-column half; the
+// hardware hands lane j column j of those four rows.
+template <int D>
+__device__ __forceinline__ bf16x8_t lds_read_tr(const uint16_t* tile, int k0, int col0, int lane) {
+  const int i = lane & 15, h = (lane >> 4) & 1, g = lane >> 5;
+  const int col = col0 + 16 * h + 4 * (i & 3);
+  const int r0 = k0 + 4 * g + (i >> 2);
+  const char* base = reinterpret_cast<const char*>(tile) + r0 * tile_rowb<D>() + col * 2;
+  i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(base));
+  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(base + 8 * tile_rowb<D>()));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 }  // namespace cpattn

@@ -334,72 +334,131 @@ def share(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: floa
     return outd
 
 
-def share_rows_forward(q_bits, k_bits, v_bits, cu, cup, cp: int, r: int, scale: float,
-                       local_rows, heads):
-    """out and lse of selected local rows / heads of rank r's share.
+class _HeadCache:
+    """float64 copies of one KV head's keys and values, converted on first use."""
 
-    Each (row, head) is one full softmax row, computed on its own, so single
-    entries of a large share can be checked without the whole share.
-    Returns out [n_rows, n_heads, D] and lse [n_heads, n_rows].
+    def __init__(self, k_bits, v_bits):
+        self.k_bits, self.v_bits = k_bits, v_bits
+        self.g = None
+
+    def get(self, g):
+        if self.g != g:
+            self.k = bf16_to_f64(self.k_bits[:, g])
+            self.v = bf16_to_f64(self.v_bits[:, g])
+            self.g = g
+        return self.k, self.v
+
+
+def _row_position(cu, cup, g_row):
+    """(sequence, in-sequence position) of a global row, or None for padding."""
+    b = int(np.searchsorted(np.asarray(cup), g_row, side="right") - 1)
+    p = g_row - int(cup[b])
+    if p >= int(cu[b + 1] - cu[b]):
+        return None
+    return b, p
+
+
+def share_rows(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
+               local_rows, heads, want_dq: bool = False):
+    """out, lse (and dQ) of selected local rows / heads of rank r's share.
+
+    Each (row, head) is one full softmax row over the keys 0..p of its
+    sequence, computed on its own, so single entries of a large share can be
+    checked without computing the whole share. dQ_p needs only row p's
+    softmax and D_p = <dO_p, out_p>.
+    Returns out [n_rows, n_heads, D], lse [n_heads, n_rows] and dq (or None).
     """
     cu, cup = validate(cu, cup, cp, r)
     own = shard_rows(cu, cup, cp, r)
-    vm = valid_mask(cu, cup)
-    hq = q_bits.shape[1]
-    hkv = k_bits.shape[1]
-    group = hq // hkv
-    d = q_bits.shape[2]
-    local_rows = np.asarray(local_rows, dtype=np.int64)
-    out = np.zeros((local_rows.size, len(heads), d))
-    lse = np.full((len(heads), local_rows.size), NEG_INF)
-    seq_of = np.searchsorted(np.asarray(cup), np.arange(int(cup[-1])), side="right") - 1
-    for i, t in enumerate(local_rows):
-        g_row = int(own[t])
-        if not vm[g_row]:
-            continue
-        b = int(seq_of[g_row])
-        base = int(cup[b])
-        p = g_row - base
-        for j, h in enumerate(heads):
-            kv = h // group
-            qh = bf16_to_f64(q_bits[g_row, h])[None, :]
-            kh = bf16_to_f64(k_bits[base:base + p + 1, kv])
-            vh = bf16_to_f64(v_bits[base:base + p + 1, kv])
-            o, l, _ = _attend_sequence(qh, kh, vh, None, np.array([p]), scale, False)
-            out[i, j] = o[0]
-            lse[j, i] = l[0]
-    return out, lse
-
-
-def share_rows_dq(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
-                  local_rows, heads):
-    """dQ of selected local rows / heads of rank r's share (each row on its own:
-    dQ_p depends only on row p's softmax and D_p = <dO_p, out_p>)."""
-    cu, cup = validate(cu, cup, cp, r)
-    own = shard_rows(cu, cup, cp, r)
-    vm = valid_mask(cu, cup)
     hq = q_bits.shape[1]
     group = hq // k_bits.shape[1]
     d = q_bits.shape[2]
     local_rows = np.asarray(local_rows, dtype=np.int64)
-    dq = np.zeros((local_rows.size, len(heads), d))
-    seq_of = np.searchsorted(np.asarray(cup), np.arange(int(cup[-1])), side="right") - 1
-    for i, t in enumerate(local_rows):
-        g_row = int(own[t])
-        if not vm[g_row]:
-            continue
-        b = int(seq_of[g_row])
-        base = int(cup[b])
-        p = g_row - base
-        for j, h in enumerate(heads):
-            kv = h // group
+    heads = list(heads)
+    out = np.zeros((local_rows.size, len(heads), d))
+    lse = np.full((len(heads), local_rows.size), NEG_INF)
+    dq = np.zeros((local_rows.size, len(heads), d)) if want_dq else None
+    cache = _HeadCache(k_bits, v_bits)
+    order = sorted(range(len(heads)), key=lambda j: heads[j] // group)
+    for j in order:
+        h = heads[j]
+        kf, vf = cache.get(h // group)
+        for i, t in enumerate(local_rows):
+            g_row = int(own[t])
+            pos = _row_position(cu, cup, g_row)
+            if pos is None:
+                continue
+            b, p = pos
+            base = int(cup[b])
             qh = bf16_to_f64(q_bits[g_row, h])[None, :]
-            doh = bf16_to_f64(do_bits[g_row, h])[None, :]
-            kh = bf16_to_f64(k_bits[base:base + p + 1, kv])
-            vh = bf16_to_f64(v_bits[base:base + p + 1, kv])
-            _, _, gr = _attend_sequence(qh, kh, vh, doh, np.array([p]), scale, True)
-            dq[i, j] = gr[0][0]
-    return dq
+            doh = bf16_to_f64(do_bits[g_row, h])[None, :] if want_dq else None
+            o, l, gr = _attend_sequence(qh, kf[base:base + p + 1], vf[base:base + p + 1], doh,
+                                        np.array([p]), scale, want_dq)
+            out[i, j] = o[0]
+            lse[j, i] = l[0]
+            if want_dq:
+                dq[i, j] = gr[0][0]
+    return out, lse, dq
+
+
+def share_rows_forward(q_bits, k_bits, v_bits, cu, cup, cp: int, r: int, scale: float, local_rows, heads):
+    """out [n_rows, n_heads, D] and lse [n_heads, n_rows] of selected rows."""
+    o, l, _ = share_rows(q_bits, k_bits, v_bits, None, cu, cup, cp, r, scale, local_rows, heads)
+    return o, l
+
+
+def share_rows_dq(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float, local_rows, heads):
+    """dQ [n_rows, n_heads, D] of selected rows."""
+    return share_rows(q_bits, k_bits, v_bits, do_bits, cu, cup, cp, r, scale, local_rows, heads, True)[2]
+
+
+def share_keys_dkdv(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
+                    shard: int, key_local_rows, kv_heads):
+    """Exact dK / dV rows of shard `shard`'s part of rank r's share, for the
+    selected local key rows and KV heads: the sum over rank r's valid query
+    rows p at or after the key, and over the query heads of the KV group, of
+    scale * dS_pj * Q_p and P_pj * dO_p. Every query row needs its own full
+    softmax row (for lse_p and D_p), so this is cheap only for keys that few
+    of the rank's queries reach (e.g. the last rows of a sequence).
+    Returns dk, dv: [n_keys, n_kv_heads, D].
+    """
+    cu, cup = validate(cu, cup, cp, r)
+    rank_of, _ = owner_map(cu, cup, cp)
+    krows = shard_rows(cu, cup, cp, shard)
+    hq = q_bits.shape[1]
+    hkv = k_bits.shape[1]
+    group = hq // hkv
+    d = q_bits.shape[2]
+    key_local_rows = np.asarray(key_local_rows, dtype=np.int64)
+    dk = np.zeros((key_local_rows.size, len(kv_heads), d))
+    dv = np.zeros((key_local_rows.size, len(kv_heads), d))
+    cache = _HeadCache(k_bits, v_bits)
+    for jg, g in enumerate(kv_heads):
+        kf, vf = cache.get(g)
+        for i, t in enumerate(key_local_rows):
+            gk = int(krows[t])
+            pos = _row_position(cu, cup, gk)
+            if pos is None:
+                continue
+            b, pk = pos
+            base = int(cup[b])
+            L = int(cu[b + 1] - cu[b])
+            for p in range(pk, L):
+                if rank_of[base + p] != r:
+                    continue
+                for h in range(g * group, (g + 1) * group):
+                    qh = bf16_to_f64(q_bits[base + p, h])[None, :]
+                    doh = bf16_to_f64(do_bits[base + p, h])[None, :]
+                    o, l, _ = _attend_sequence(qh, kf[base:base + p + 1], vf[base:base + p + 1], None,
+                                               np.array([p]), scale, False)
+                    s_pj = scale * float(qh[0] @ kf[base + pk])
+                    p_pj = np.exp(s_pj - l[0])
+                    dp = float(doh[0] @ vf[base + pk])
+                    dcoef = float(doh[0] @ o[0])
+                    ds = p_pj * (dp - dcoef)
+                    dk[i, jg] += scale * ds * qh[0]
+                    dv[i, jg] += p_pj * doh[0]
+    return dk, dv
 
 
 def flops_share(cu, cup, cp: int, r: int, hq: int, d: int) -> dict:

@@ -1,0 +1,132 @@
+"""Parity at the full sizes the benchmark runs (the 131072-token GQA share and
+the 64K hierarchical-pack share), in the same launch configuration.
+
+The whole share is too large for the oracle, so: out / LSE / dQ are checked on
+sampled rows (each row one full softmax row of the oracle), dK / dV exactly on
+key rows that few of the rank's queries reach, every part's rows that no query
+of the rank reaches must be exactly zero, and four identities that hold at any
+size tie all rows of all parts together:
+  sum_j dV_j = sum_p dO_p            (softmax rows sum to one)
+  sum_j dK_j = 0                     (softmax is shift invariant)
+  sum_p <dQ_p, Q_p> = sum_j <dK_j, K_j>   (both equal scale * sum dS_pj s_pj)
+  sum_p <dO_p, out_p> = sum_j <dV_j, V_j>
+each per KV head, summed over the query heads of its group.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from context_packed_attention_amd import synth
+from oracle import cp_attn_oracle as O
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg):
+    bt, w = synth.make_workload(cfg)
+    r = w["ranks"][-1]
+    cp = w["cp"]
+    scale = 1.0 / math.sqrt(bt.d)
+    H.log(f"[full] {bt.name} cp={cp} rank={r}: GPU fwd+bwd")
+    db = H.DeviceBatch(bt)
+    meta, loc = H.local_inputs(db, cp, r)
+    out, lse = H.run_fwd(meta, loc, bt, scale)
+    dq, dks, dvs = H.run_bwd(meta, loc, bt, scale, out, lse)
+    res = {"out": H.bf16_to_np(out), "lse": lse.cpu().numpy(), "dq": H.bf16_to_np(dq),
+           "dk": [H.bf16_to_np(x) for x in dks], "dv": [H.bf16_to_np(x) for x in dvs],
+           "q": H.bf16_to_np(loc["q"]), "do": H.bf16_to_np(loc["do"]),
+           "k": [H.bf16_to_np(x) for x in loc["k"]], "v": [H.bf16_to_np(x) for x in loc["v"]]}
+    meta.close()
+    del db
+    return bt, w, r, scale, res
+
+
+def _sample_rows(T_local, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 127, 128, T_local // 2 - 1, T_local // 2, T_local // 2 + 1, T_local - 2, T_local - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, T_local, n)]))
+
+
+@pytest.fixture(scope="module", params=[4, 5], ids=["single131072-gqa-cp4", "pack64k-hier2x2-p2p"])
+def full(request):
+    return _run(request.param)
+
+
+def test_sampled_rows_out_lse_dq(full):
+    bt, w, r, scale, res = full
+    T_local = bt.total_rows // w["cp"]
+    rows = _sample_rows(T_local, 24, 7)
+    heads = sorted({0, bt.hq - 1, bt.hq // 2, 3 % bt.hq})
+    H.log(f"[full] oracle rows={rows.size} heads={heads}")
+    o, l, dq = O.share_rows(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, w["cp"], r, scale, rows, heads, want_dq=True)
+    H.compare_bf16("out", res["out"][rows][:, heads], o)
+    H.compare_lse("lse", res["lse"][heads][:, rows], l)
+    H.compare_bf16("dq", res["dq"][rows][:, heads], dq)
+
+
+def test_exact_key_rows_and_zero_rows(full):
+    bt, w, r, scale, res = full
+    cp = w["cp"]
+    T_local = bt.total_rows // cp
+    own_rows = O.shard_rows(bt.cu, bt.cup, cp, r)
+    # the last few local rows of the rank's last sequence: few queries reach them
+    keys = np.arange(T_local - 12, T_local)
+    kvh = [0, bt.hkv - 1]
+    H.log(f"[full] oracle dK/dV for {keys.size} key rows")
+    dk, dv = O.share_keys_dkdv(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, r, keys, kvh)
+    H.compare_bf16("dk rows", res["dk"][r][keys][:, kvh], dk)
+    H.compare_bf16("dv rows", res["dv"][r][keys][:, kvh], dv)
+    # rows of each part that no query of this rank reaches are exactly zero
+    rank_of, _ = O.owner_map(bt.cu, bt.cup, cp)
+    seq = np.searchsorted(bt.cup, np.arange(bt.total_rows), side="right") - 1
+    valid = O.valid_mask(bt.cu, bt.cup)
+    last_q = np.full(bt.cu.size - 1, -1)
+    for g in np.nonzero((rank_of == r) & valid)[0]:
+        last_q[seq[g]] = max(last_q[seq[g]], g)
+    for s in range(cp):
+        rows = O.shard_rows(bt.cu, bt.cup, cp, s)
+        unreached = ~valid[rows] | (rows > last_q[seq[rows]])
+        assert not res["dk"][s][unreached].any() and not res["dv"][s][unreached].any(), s
+
+
+def _tol(vals):
+    return 1e-3 * np.sqrt((vals ** 2).sum()) + 1e-6
+
+
+def test_gradient_identities(full):
+    bt, w, r, scale, res = full
+    cp = w["cp"]
+    group = bt.hq // bt.hkv
+    f = H.bf16_bits_to_f64
+    q = f(res["q"])
+    do = f(res["do"])
+    dq = f(res["dq"])
+    out = f(res["out"])
+    own = O.shard_rows(bt.cu, bt.cup, cp, r)
+    valid_q = O.valid_mask(bt.cu, bt.cup)[own]
+    for g in range(bt.hkv):
+        hs = slice(g * group, (g + 1) * group)
+        sum_dv = sum(f(res["dv"][s][:, g]).sum(axis=0) for s in range(cp))
+        ref_dv = do[valid_q, hs].sum(axis=(0, 1))
+        err = np.abs(sum_dv - ref_dv).max()
+        assert err <= _tol(ref_dv) + 0.05, (g, err)
+        # sum_j dS_pj vanishes only up to the rounding of D_p = <dO_p, out_p>
+        # (taken from the bf16 output): e_p ~ 2^-8 * sum_d |dO out|, so the
+        # d-th component of sum_j dK_j is a random sum with standard deviation
+        # scale * sqrt(sum_p Q_pd^2 e_p^2), plus the bf16 rounding of the dK rows.
+        sum_dk = sum(f(res["dk"][s][:, g]).sum(axis=0) for s in range(cp))
+        e = 2.0 ** -8 * np.abs(do[valid_q, hs] * out[valid_q, hs]).sum(axis=-1)        # [rows, group]
+        std = scale * np.sqrt(((q[valid_q, hs] ** 2) * (e ** 2)[..., None]).sum(axis=(0, 1)))
+        rnd = 2.0 ** -9 * np.sqrt(sum((f(res["dk"][s][:, g]) ** 2).sum(axis=0) for s in range(cp)))
+        worst = float((np.abs(sum_dk) / (6 * std + 8 * rnd + 1e-6)).max())
+        assert worst <= 1.0, (g, float(np.abs(sum_dk).max()), worst)
+        lhs = float((dq[valid_q, hs] * q[valid_q, hs]).sum())
+        rhs = sum(float((f(res["dk"][s][:, g]) * f(res["k"][s][:, g])).sum()) for s in range(cp))
+        mag = math.sqrt(float((dq[valid_q, hs] ** 2).sum()) * float((q[valid_q, hs] ** 2).sum()))
+        assert abs(lhs - rhs) <= 1e-3 * mag + 1e-3, (g, lhs, rhs)
+        lhs2 = float((do[valid_q, hs] * out[valid_q, hs]).sum())
+        rhs2 = sum(float((f(res["dv"][s][:, g]) * f(res["v"][s][:, g])).sum()) for s in range(cp))
+        mag2 = math.sqrt(float((do[valid_q, hs] ** 2).sum()) * float((out[valid_q, hs] ** 2).sum()))
+        assert abs(lhs2 - rhs2) <= 1e-3 * mag2 + 1e-3, (g, lhs2, rhs2)

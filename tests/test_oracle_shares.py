@@ -153,3 +153,32 @@ def test_unmutated_oracle_passes_pins():
 @pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(label, old, new):
     assert not _pins_pass(_mutant(old, new)), label
+
+
+def test_key_rows_match_full_share():
+    bt = _random_batch(9, 2, 3, 4, 2, 8, True)
+    scale = 0.33
+    for r in range(2):
+        sh = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, 2, r, scale)
+        for s in range(2):
+            keys = np.arange(bt.total_rows // 2)
+            dk, dv = O.share_keys_dkdv(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, 2, r, scale, s, keys, [0, 1])
+            np.testing.assert_allclose(dk, sh["dk_parts"][s], rtol=1e-11, atol=1e-11)
+            np.testing.assert_allclose(dv, sh["dv_parts"][s], rtol=1e-11, atol=1e-11)
+
+
+def test_dropped_ring_steps_would_fail_parity():
+    """A share computed from the rank's own shard only (every ring step after
+    the first dropped) is far outside the parity tolerance on the tiny pack,
+    so the GPU parity tests detect a path that skips the exchange."""
+    bt, w = synth.make_workload(1)
+    scale = 1 / np.sqrt(bt.d)
+    for r in (0, 1):
+        full = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, 2, r, scale)
+        rows = O.shard_rows(bt.cu, bt.cup, 2, r)
+        md = O.rank_metadata(bt.cu, bt.cup, 2, r)
+        cu_loc = md[f"cu_full_{r}"]
+        sub = lambda x: O.bf16_to_f64(x[rows])
+        own = O.attention(sub(bt.q), sub(bt.k), sub(bt.v), sub(bt.do), cu_loc, md["cu_padded_local"], scale)
+        assert np.abs(own[0] - full["out"]).max() > 0.2
+        assert np.abs(own[2] - full["dq"]).max() > 0.2
