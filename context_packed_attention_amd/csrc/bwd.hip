@@ -80,8 +80,8 @@ template <int D>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, BN>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, BN>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, false, BN>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, false, BN>() / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   auto issue = [&](int kt, int buf) {
-    load_tile_lds<D, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
-    load_tile_lds<D, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, false, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, false, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
   };
   if (nt > 0) issue(0, 0);
 
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
         const bf16x8_t ds = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
         for (int md = 0; md < NMD; ++md)
-          acc[md] = mfma32x32x16(lds_read_tr<D>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
+          acc[md] = mfma32x32x16(lds_read_tr<D, false>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
       }
     }
   }
@@ -202,9 +202,9 @@ template <int D>
 __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][tile_bytes<D, BQ>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][tile_bytes<D, BQ>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vt[tile_bytes<D, BK>() / 2];  // the block's V rows
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][tile_bytes<D, false, BQ>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][tile_bytes<D, false, BQ>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vt[tile_bytes<D, false, BK>() / 2];  // the block's V rows
   __shared__ __attribute__((aligned(16))) float LD[2][2 * BQ];  // per buffer: LSE rows, then D rows
 
   const int tid = threadIdx.x;
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
       const int ldkv = (int)(p.ld_kv * 2);
       const __amdgpu_buffer_rsrc_t vrs =
           make_rsrc(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, (long long)nk * ldkv);
-      load_tile_lds<D, BK>(vrs, Vt, 0, ldkv, w, lane);
+      load_tile_lds<D, false, BK>(vrs, Vt, 0, ldkv, w, lane);
     }
     const int ldb = (int)(p.ld_q * 2);
     const long long range = (long long)ql * ldb;
@@ -256,8 +256,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
       const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + (long long)qs * p.ld_q + hh * D, range);
       const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse + (long long)hh * p.ld_lse + qs, (long long)ql * 4);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.dvec + (long long)hh * p.ld_d + qs, (long long)ql * 4);
-      load_tile_lds<D, BQ>(qr, Qs[buf], qt * BQ * ldb, ldb, w, lane);
-      load_tile_lds<D, BQ>(dr, Ds[buf], qt * BQ * ldb, ldb, w, lane);
+      load_tile_lds<D, false, BQ>(qr, Qs[buf], qt * BQ * ldb, ldb, w, lane);
+      load_tile_lds<D, false, BQ>(dr, Ds[buf], qt * BQ * ldb, ldb, w, lane);
       if (w == 0) {
         // lane l writes LDS bytes [16 l, 16 l + 16) of LD[buf]: lanes 0..7 the
         // tile's LSE rows, lanes 8..15 its D rows (4 rows per lane)
@@ -318,8 +318,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
           const bf16x8_t db = pack8_bf16(dp, 8 * kq);
 #pragma unroll
           for (int md = 0; md < NMD; ++md) {
-            dv[md] = mfma32x32x16(lds_read_tr<D>(Ds[buf], kq * 16, md * 32, lane), pb, dv[md]);
-            dk[md] = mfma32x32x16(lds_read_tr<D>(Qs[buf], kq * 16, md * 32, lane), db, dk[md]);
+            dv[md] = mfma32x32x16(lds_read_tr<D, false>(Ds[buf], kq * 16, md * 32, lane), pb, dv[md]);
+            dk[md] = mfma32x32x16(lds_read_tr<D, false>(Qs[buf], kq * 16, md * 32, lane), db, dk[md]);
           }
         }
       }

@@ -53,8 +53,8 @@ __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
   static_assert(BM == 128, "4 wavefronts x 32 rows");
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, BN>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, BN>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, false, BN>() / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, true, BN>() / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -92,8 +92,8 @@ __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   auto issue = [&](int kt, int buf) {
-    load_tile_lds<D, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
-    load_tile_lds<D, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, false, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, true, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
   };
 
   if (nt > 0) issue(0, 0);
@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
         const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
         for (int md = 0; md < NMD; ++md)
-          o[md] = mfma32x32x16(lds_read_tr<D>(Vs[buf], kk2 * 16, md * 32, lane), pb, o[md]);
+          o[md] = mfma32x32x16(lds_read_tr<D, true>(Vs[buf], kk2 * 16, md * 32, lane), pb, o[md]);
       }
     }
   }

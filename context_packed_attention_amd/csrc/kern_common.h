@@ -105,18 +105,24 @@ __device__ __forceinline__ void map_block(int bid, int nheads, int& item, int& h
 }
 
 // ---------------------------------------------------------------- LDS tiles
-// Row-major tiles (rows x D bf16) live in LDS with padded rows: 304 bytes per
-// row for D = 128 (19 units of 16 bytes, 16 used) and 144 bytes for D = 64
-// (9 units, 8 used). On gfx950's 64-bank LDS (16 lanes served per cycle for
-// b128 and b64 reads) these strides keep both access patterns conflict-free
-// while every address stays linear in the unrolled loop indices:
-//  * b128 operand reads, where 16 lanes read one unit of 16 consecutive rows;
-//  * ds_read_b64_tr_b16 transposed reads, where a 16-lane group reads 4
-//    consecutive rows (first row a multiple of 4) x 32 consecutive bytes.
-template <int D>
-__host__ __device__ constexpr int tile_rowb() { return D == 128 ? 304 : 144; }
-template <int D, int ROWS>
-__host__ __device__ constexpr int tile_bytes() { return ROWS * tile_rowb<D>(); }
+// Row-major tiles (rows x D bf16) live in LDS with padded rows. gfx950's LDS
+// has 64 banks of 4 bytes; a b128 read serves 16 lanes per cycle and the
+// transposing ds_read_b64_tr_b16 serves 32 lanes per cycle. Row strides:
+//  * tiles read by b128 row reads (16 lanes = one 16-byte unit of 16
+//    consecutive rows), alone or together with transposing reads: 304 bytes
+//    (D = 128) or 144 (D = 64) - conflict-free for the row reads, while a
+//    transposing read pays about 1.6 extra cycles;
+//  * tiles read only by transposing reads (32 lanes take 64 consecutive bytes
+//    of 4 consecutive rows, first row a multiple of 4): 320 bytes (D = 128)
+//    or 192 (D = 64) - conflict-free.
+// Padding (no XOR swizzle) keeps every address linear in the unrolled loop
+// indices, so the compiler folds them into instruction offsets; a swizzle
+// that removed both kinds of conflict measured slower for its extra address
+// arithmetic.
+template <int D, bool TR_ONLY>
+__host__ __device__ constexpr int tile_rowb() { return TR_ONLY ? (D == 128 ? 320 : 192) : (D == 128 ? 304 : 144); }
+template <int D, bool TR_ONLY, int ROWS>
+__host__ __device__ constexpr int tile_bytes() { return ROWS * tile_rowb<D, TR_ONLY>(); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -135,15 +141,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 constexpr int OOB_OFFSET = 0x7ffffff0;  // any offset past num_records reads zeros
 
 // Copy one tile of ROWS x D bf16 (global rows `ld_bytes` apart, starting at
-// byte `row0_off` of the resource) into a padded LDS tile. The tile is filled
-// as a linear run of 16-byte units in 1 KB chunks shared by the block's 4
-// wavefronts; a lane whose unit is row padding loads zeros, lanes past the
-// tile's end stay idle.
-template <int D, int ROWS>
+// byte `row0_off` of the resource) into a padded LDS tile. The
+// tile is filled as a linear run of 16-byte units in 1 KB chunks shared by
+// the block's 4 wavefronts; a lane whose unit is row padding loads zeros,
+// lanes past the tile's end stay idle.
+template <int D, bool TR_ONLY, int ROWS>
 __device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, int row0_off,
                                               int ld_bytes, int wave, int lane) {
-  constexpr int SU = tile_rowb<D>() / 16;   // units per padded row
-  constexpr int UPR = D * 2 / 16;           // units per data row
+  constexpr int SU = tile_rowb<D, TR_ONLY>() / 16;  // units per padded row
+  constexpr int UPR = D * 2 / 16;              // units per data row
   constexpr int UNITS = ROWS * SU;
   constexpr int CHUNKS = (UNITS + 63) / 64;
 #pragma unroll
@@ -158,10 +164,11 @@ __device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t rsrc, uint1
   }
 }
 
-// b128 read of 16-byte unit `unit` of `row`.
+// b128 read of 16-byte unit `unit` of `row` (tiles with row reads).
 template <int D>
 __device__ __forceinline__ bf16x8_t lds_read_row(const uint16_t* tile, int row, int unit) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + row * tile_rowb<D>() + unit * 16));
+  return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + row * tile_rowb<D, false>() +
+                                                   unit * 16));
 }
 
 // Transposed operand (ds_read_b64_tr_b16) for the 32-wide MFMA A operand
@@ -170,15 +177,15 @@ __device__ __forceinline__ bf16x8_t lds_read_row(const uint16_t* tile, int row, 
 // a multiple of 16). Within each 16-lane group, lane j supplies the address
 // of row (first + j / 4), columns 4 (j % 4) .. +3 of its 16-column half; the
 // hardware hands lane j column j of those four rows.
-template <int D>
+template <int D, bool TR_ONLY>
 __device__ __forceinline__ bf16x8_t lds_read_tr(const uint16_t* tile, int k0, int col0, int lane) {
+  constexpr int ROWB = tile_rowb<D, TR_ONLY>();
   const int i = lane & 15, h = (lane >> 4) & 1, g = lane >> 5;
   const int col = col0 + 16 * h + 4 * (i & 3);
   const int r0 = k0 + 4 * g + (i >> 2);
-  const char* base = reinterpret_cast<const char*>(tile) + r0 * tile_rowb<D>() + col * 2;
+  const char* base = reinterpret_cast<const char*>(tile) + r0 * ROWB + col * 2;
   i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(base));
-  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4_t*)(base + 8 * tile_rowb<D>()));
+  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(base + 8 * ROWB));
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
