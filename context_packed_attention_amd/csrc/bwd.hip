@@ -70,14 +70,14 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
   }
 }
 
-// dQ of one ring step. Block = 4 wavefronts x 32 query rows of one head;
+// dQ of one ring step. Block = NWAVES wavefronts x 32 query rows of one head;
 // key tiles of 64 rows: K and V are copied straight into padded LDS tiles
 // (double-buffered). Row-major reads of K and V feed the transposed scores
 // S^T = K Q^T and dP^T = V dO^T (lane = one query row); transposing reads of
 // the same K tile feed dQ^T = K^T dS^T. Keys past the step's key range read as
 // zeros, so their K^T rows contribute nothing and need no mask.
 template <int D>
-__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdParams p) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, false, BN>() / 2];
@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   auto issue = [&](int kt, int buf) {
-    load_tile_lds<D, false, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
-    load_tile_lds<D, false, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, false, BN, NWAVES>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, false, BN, NWAVES>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
   };
   if (nt > 0) issue(0, 0);
 
@@ -187,8 +187,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
   }
 }
 
-// dK/dV of one ring step for the source shard's key rows. Block = 4
-// wavefronts x 32 key rows of one KV head (DKDV_BN = 128 keys), K in
+// dK/dV of one ring step for the source shard's key rows. Block = NWAVES
+// wavefronts x 32 key rows of one KV head (DKDV_BN keys), K in
 // registers and V in LDS; loops over the query heads of the group and the step's query rows
 // in tiles of 32. Q and dO tiles are copied straight into padded LDS tiles
 // (double-buffered) together with the rows' LSE and D. Row-major reads feed
@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 // are computed but written as zeros. Rows of the part outside the step's key
 // range are written as zeros too, so the whole shard-s part is defined.
 template <int D>
-__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][tile_bytes<D, false, BQ>() / 2];
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
       const int ldkv = (int)(p.ld_kv * 2);
       const __amdgpu_buffer_rsrc_t vrs =
           make_rsrc(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, (long long)nk * ldkv);
-      load_tile_lds<D, false, BK>(vrs, Vt, 0, ldkv, w, lane);
+      load_tile_lds<D, false, BK, NWAVES>(vrs, Vt, 0, ldkv, w, lane);
     }
     const int ldb = (int)(p.ld_q * 2);
     const long long range = (long long)ql * ldb;
@@ -256,8 +256,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
       const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + (long long)qs * p.ld_q + hh * D, range);
       const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse + (long long)hh * p.ld_lse + qs, (long long)ql * 4);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.dvec + (long long)hh * p.ld_d + qs, (long long)ql * 4);
-      load_tile_lds<D, false, BQ>(qr, Qs[buf], qt * BQ * ldb, ldb, w, lane);
-      load_tile_lds<D, false, BQ>(dr, Ds[buf], qt * BQ * ldb, ldb, w, lane);
+      load_tile_lds<D, false, BQ, NWAVES>(qr, Qs[buf], qt * BQ * ldb, ldb, w, lane);
+      load_tile_lds<D, false, BQ, NWAVES>(dr, Ds[buf], qt * BQ * ldb, ldb, w, lane);
       if (w == 0) {
         // lane l writes LDS bytes [16 l, 16 l + 16) of LD[buf]: lanes 0..7 the
         // tile's LSE rows, lanes 8..15 its D rows (4 rows per lane)
@@ -481,9 +481,9 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
         p.items = m->d_tab + m->lay.dkdv_tiles + (int64_t)i * m->lay.dkdv_cap * 2;
         timing_begin(st, "bwd_dkdv");
         if (d == 128)
-          hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nkv), dim3(256), 0, st, p);
+          hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, st, p);
         else
-          hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nkv), dim3(256), 0, st, p);
+          hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, st, p);
         timing_end(st);
         if ((rc = hip_check(hipGetLastError(), "bwd_dkdv launch")) != CP_ATTN_OK) return rc;
       }
@@ -492,9 +492,9 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
         p.items = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
         timing_begin(st, "bwd_dq");
         if (d == 128)
-          hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(256), 0, st, p);
+          hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(BLOCK_THREADS), 0, st, p);
         else
-          hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(256), 0, st, p);
+          hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(BLOCK_THREADS), 0, st, p);
         timing_end(st);
         if ((rc = hip_check(hipGetLastError(), "bwd_dq launch")) != CP_ATTN_OK) return rc;
       }

@@ -37,7 +37,7 @@ struct FwdParams {
   long long ld_o, ld_lse;
 };
 
-// One block = 4 wavefronts = 128 query rows of one head; each wavefront owns
+// One block = NWAVES wavefronts (FWD_BM query rows) of one head; each wavefront owns
 // 32 query rows. K and V tiles of 64 rows are copied straight from global
 // memory into padded LDS tiles (buffer loads with the lds modifier, no
 // register staging), double-buffered. Scores are computed transposed
@@ -48,11 +48,10 @@ struct FwdParams {
 // Rescaling is lazy: the running max only moves when a tile's max exceeds it
 // by more than 2^8 in exp2 units.
 template <int D>
-__global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
+__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(FwdParams p) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
-  static_assert(BM == 128, "4 wavefronts x 32 rows");
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, false, BN>() / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, true, BN>() / 2];
 
@@ -92,8 +91,8 @@ __global__ void __launch_bounds__(256, 2) fwd_step_kernel(FwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
   auto issue = [&](int kt, int buf) {
-    load_tile_lds<D, false, BN>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
-    load_tile_lds<D, true, BN>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, false, BN, NWAVES>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
+    load_tile_lds<D, true, BN, NWAVES>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
   };
 
   if (nt > 0) issue(0, 0);
@@ -265,9 +264,9 @@ static cp_attn_status launch_fwd_step(const cp_attn_meta* m, int i, const FwdPar
   if (blocks > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
   timing_begin(st, "fwd_step");
   if (d == 128)
-    hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, st, p);
   else
-    hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, st, p);
   timing_end(st);
   return hip_check(hipGetLastError(), "fwd_step launch");
 }

@@ -11,10 +11,17 @@
 namespace cpattn {
 
 // ---------------------------------------------------------------- tiling
-// Query rows per forward / dQ work item (4 wavefronts x 32 rows).
-constexpr int FWD_BM = 128;
-// Key rows per dK/dV work item (4 wavefronts x 32 keys).
-constexpr int DKDV_BN = 128;
+// Wavefronts per block of the attention kernels; each owns 32 query rows
+// (forward, dQ) or 32 key rows (dK/dV).
+#ifndef CPA_NWAVES
+#define CPA_NWAVES 4
+#endif
+constexpr int NWAVES = CPA_NWAVES;
+constexpr int BLOCK_THREADS = 64 * NWAVES;
+// Query rows per forward / dQ work item.
+constexpr int FWD_BM = 32 * NWAVES;
+// Key rows per dK/dV work item.
+constexpr int DKDV_BN = 32 * NWAVES;
 // Work lists up to this length are sorted heaviest-first on the device.
 constexpr int SORT_CAP = 4096;
 

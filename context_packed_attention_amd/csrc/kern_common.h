@@ -143,9 +143,9 @@ constexpr int OOB_OFFSET = 0x7ffffff0;  // any offset past num_records reads zer
 // Copy one tile of ROWS x D bf16 (global rows `ld_bytes` apart, starting at
 // byte `row0_off` of the resource) into a padded LDS tile. The
 // tile is filled as a linear run of 16-byte units in 1 KB chunks shared by
-// the block's 4 wavefronts; a lane whose unit is row padding loads zeros,
+// the block's NW wavefronts; a lane whose unit is row padding loads zeros,
 // lanes past the tile's end stay idle.
-template <int D, bool TR_ONLY, int ROWS>
+template <int D, bool TR_ONLY, int ROWS, int NW>
 __device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, int row0_off,
                                               int ld_bytes, int wave, int lane) {
   constexpr int SU = tile_rowb<D, TR_ONLY>() / 16;  // units per padded row
@@ -153,10 +153,10 @@ __device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t rsrc, uint1
   constexpr int UNITS = ROWS * SU;
   constexpr int CHUNKS = (UNITS + 63) / 64;
 #pragma unroll
-  for (int cc = 0; cc < (CHUNKS + 3) / 4; ++cc) {
-    const int c = cc * 4 + wave;
+  for (int cc = 0; cc < (CHUNKS + NW - 1) / NW; ++cc) {
+    const int c = cc * NW + wave;
     const int u = c * 64 + lane;
-    if ((CHUNKS % 4 == 0 || c < CHUNKS) && (UNITS % 64 == 0 || u < UNITS)) {
+    if ((CHUNKS % NW == 0 || c < CHUNKS) && (UNITS % 64 == 0 || u < UNITS)) {
       const int row = u / SU, unit = u % SU;
       const int off = unit < UPR ? row0_off + row * ld_bytes + unit * 16 : OOB_OFFSET;
       load_lds16(rsrc, reinterpret_cast<char*>(lds_tile) + c * 1024, off);
