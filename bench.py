@@ -44,7 +44,23 @@ def parse():
                     help="1..5: tiny / 16K pack / padded 16K pack / 131072-token GQA / 64K hierarchical pack")
     ap.add_argument("--cpu-sample-stride", type=int, default=256,
                     help="oracle baseline: every Nth query row of the share (0 = skip the baseline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times and exit "
+                         "(the known-size reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(batch, w, rank, scale, stride):
@@ -106,6 +122,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     w = synth.workload(args.workload)
     rank = w["ranks"][-1] if args.workload != 1 else 0
     log(f"[bench] drawing inputs for {w['name']}")

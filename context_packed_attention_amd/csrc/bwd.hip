@@ -23,9 +23,8 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;   // forward LSE [hq, ld_lse]
-  const float* dvec;  // D = rowsum(dO * out) [hq, ld_d]
-  long long ld_lse, ld_d;
+  const float* ldv;   // per (head, local row): (lse * log2(e), D), fp32 pairs [hq, ld_ldv, 2]
+  long long ld_ldv;
   const int32_t* q_start;
   const int32_t* q_len;
   const int32_t* kv_start;
@@ -42,10 +41,13 @@ struct BwdParams {
   uint16_t* dv;
 };
 
-// D = rowsum(dO * out) per (row, head), fp32 [hq, t_local]; 0 on padding rows.
-// 16 lanes cover one (row, head) of D = 128 (8 lanes for D = 64).
+// Per (head, local row): the forward's LSE in exp2 units and
+// D = rowsum(dO * out), as an fp32 pair [hq, t_local, 2]; padding rows get
+// (+inf, 0), so their probabilities vanish. 16 lanes cover one (row, head) of
+// D = 128 (8 lanes for D = 64).
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ out,
-                                                      const int32_t* __restrict__ rowflags, float* __restrict__ dvec,
+                                                      const float* __restrict__ lse, long long ld_lse,
+                                                      const int32_t* __restrict__ rowflags, float* __restrict__ ldv,
                                                       int t_local, int hq, int d) {
   const int lanes = d / 8;
   const long long n = (long long)t_local * hq * lanes;
@@ -54,8 +56,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
     const int part = (int)(e - rh * lanes);
     const int t = (int)(rh / hq);
     const int h = (int)(rh - (long long)t * hq);
+    const bool valid = rowflags[t] & RF_VALID;
     float acc = 0.f;
-    if (rowflags[t] & RF_VALID) {
+    if (valid) {
       const uint4 a = *reinterpret_cast<const uint4*>(dout + rh * d + part * 8);
       const uint4 b = *reinterpret_cast<const uint4*>(out + rh * d + part * 8);
 #pragma unroll
@@ -66,7 +69,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
       }
     }
     for (int off = lanes >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (part == 0) dvec[(long long)h * t_local + t] = acc;
+    if (part == 0) {
+      const float l2 = valid ? lse[(long long)h * ld_lse + t] * LOG2E_F : __builtin_huge_valf();
+      *reinterpret_cast<float2*>(ldv + ((long long)h * t_local + t) * 2) = make_float2(l2, acc);
+    }
   }
 }
 
@@ -80,8 +86,9 @@ template <int D>
 __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdParams p) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, false, BN>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, false, BN>() / 2];
+  using KCopy = TileCopy<D, false, BN, NWAVES>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][KCopy::BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][KCopy::BYTES / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -108,20 +115,24 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
       df[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p.dout + roff + kk * 16) : make_uint4(0, 0, 0, 0));
     }
   }
-  const float lse2 = qok ? p.lse[(long long)head * p.ld_lse + qs + qrow] * LOG2E_F : __builtin_huge_valf();
-  const float dq_d = qok ? p.dvec[(long long)head * p.ld_d + qs + qrow] : 0.f;
+  const float2 ld = qok ? *reinterpret_cast<const float2*>(p.ldv + ((long long)head * p.ld_ldv + qs + qrow) * 2)
+                        : make_float2(__builtin_huge_valf(), 0.f);
+  const float lse2 = ld.x, dq_d = ld.y;
 
   f32x16_t acc[NMD];
 #pragma unroll
   for (int md = 0; md < NMD; ++md) acc[md] = zero16();
 
   const int ldb = (int)(p.ld_kv * 2);
-  const long long range_bytes = (long long)kl * ldb;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
+  const long long kv_end = (long long)kl * ldb;
+  const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
+  const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
+  KCopy kc;
+  kc.init(ldb, w, lane);
   auto issue = [&](int kt, int buf) {
-    load_tile_lds<D, false, BN, NWAVES>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
-    load_tile_lds<D, false, BN, NWAVES>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
+    const long long off = (long long)kt * BN * ldb;
+    kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
+    kc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
   };
   if (nt > 0) issue(0, 0);
 
@@ -148,13 +159,21 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
           dp[mb] = mfma32x32x16(lds_read_row<D>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
         }
       }
-      const bool need_mask = p.causal && k0 + BN - 1 > wrow_lo;
+      if (p.causal && k0 + BN - 1 > wrow_lo) {
+        // keys after the lane's row (a real branch, kept out of
+        // if-conversion; only the tiles on a wavefront's diagonal take it)
+        __asm__ volatile("" ::: "memory");
+        const int rel = qrow - k0 - 4 * g;  // element (mb, j): key offset 32 mb + 8 (j / 4) + j % 4
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) s[mb][j] = (mb * 32 + (j >> 2) * 8 + (j & 3) <= rel) ? s[mb][j] : NEG_INF_F;
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float pv = fast_exp2(fmaf(s[mb][j], c, -lse2));
-          if (need_mask) pv = (k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3) <= qrow) ? pv : 0.f;
+          const float pv = fast_exp2(fmaf(s[mb][j], c, -lse2));
           s[mb][j] = pv * (dp[mb][j] - dq_d);  // dS^T
         }
 #pragma unroll
@@ -202,10 +221,12 @@ template <int D>
 __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][tile_bytes<D, false, BQ>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][tile_bytes<D, false, BQ>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vt[tile_bytes<D, false, BK>() / 2];  // the block's V rows
-  __shared__ __attribute__((aligned(16))) float LD[2][2 * BQ];  // per buffer: LSE rows, then D rows
+  using QCopy = TileCopy<D, false, BQ, NWAVES>;
+  using VCopy = TileCopy<D, false, BK, NWAVES>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][QCopy::BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][QCopy::BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vt[VCopy::BYTES / 2];  // the block's V rows
+  __shared__ __attribute__((aligned(16))) float LD[2][2 * BQ];  // per buffer: (lse * log2(e), D) per row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -244,30 +265,28 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
       for (int kk = 0; kk < NKK; ++kk)
         kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.k + off + kk * 16) : make_uint4(0, 0, 0, 0));
       const int ldkv = (int)(p.ld_kv * 2);
-      const __amdgpu_buffer_rsrc_t vrs =
-          make_rsrc(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, (long long)nk * ldkv);
-      load_tile_lds<D, false, BK, NWAVES>(vrs, Vt, 0, ldkv, w, lane);
+      VCopy vcp;
+      vcp.init(ldkv, w, lane);
+      vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, (long long)nk * ldkv), Vt, w);
     }
     const int ldb = (int)(p.ld_q * 2);
-    const long long range = (long long)ql * ldb;
-    // per query head of the group: resources over the step's query rows
+    const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 8;
+    QCopy qc;  // the same plan serves Q and dO
+    qc.init(ldb, w, lane);
+    // query head hh, query tile qt: Q and dO rows, and the rows' (lse, D)
+    // pairs (256 bytes, copied by 16 lanes of wavefront 0)
     auto issue = [&](int hh, int qt, int buf) {
-      const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + (long long)qs * p.ld_q + hh * D, range);
-      const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + (long long)qs * p.ld_q + hh * D, range);
-      const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse + (long long)hh * p.ld_lse + qs, (long long)ql * 4);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.dvec + (long long)hh * p.ld_d + qs, (long long)ql * 4);
-      load_tile_lds<D, false, BQ, NWAVES>(qr, Qs[buf], qt * BQ * ldb, ldb, w, lane);
-      load_tile_lds<D, false, BQ, NWAVES>(dr, Ds[buf], qt * BQ * ldb, ldb, w, lane);
+      const long long hoff = (long long)qs * p.ld_q + hh * D;
+      const long long off = (long long)qt * BQ * ldb;
+      qc.copy(rsrc_from(p.q + hoff, off, q_end), Qs[buf], w);
+      qc.copy(rsrc_from(p.dout + hoff, off, q_end), Ds[buf], w);
       if (w == 0) {
-        // lane l writes LDS bytes [16 l, 16 l + 16) of LD[buf]: lanes 0..7 the
-        // tile's LSE rows, lanes 8..15 its D rows (4 rows per lane)
-        if (lane < BQ / 4)
-          load_lds16(lr, &LD[buf][0], qt * BQ * 4 + lane * 16);
-        else if (lane < BQ / 2)
-          load_lds16(vr, &LD[buf][0], qt * BQ * 4 + (lane - BQ / 4) * 16);
+        const __amdgpu_buffer_rsrc_t lr =
+            rsrc_from(p.ldv + ((long long)hh * p.ld_ldv + qs) * 2, (long long)qt * BQ * 8, ld_end);
+        if (lane < BQ / 2) load_lds16(lr, &LD[buf][0], lane * 16);
       }
     };
-    static_assert(sizeof(LD[0]) == 2 * BQ * 4, "LSE/D layout");
+    static_assert(sizeof(LD[0]) == BQ * 8, "(lse, D) tile layout");
 
     int hh = kvh * p.group, qt = qt_begin;
     issue(hh, qt, 0);
@@ -295,18 +314,25 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
           dp = mfma32x32x16(lds_read_row<D>(Ds[buf], l32, 2 * kk + g),
                             lds_read_row<D>(Vt, w * 32 + l32, 2 * kk + g), dp);
         }
-        const bool need_mask = p.causal && qlo < wkey_hi;
+        if (p.causal && qlo < wkey_hi) {
+          // query rows before this lane's key (a real branch, kept out of
+          // if-conversion; only a wavefront's first tiles take it)
+          __asm__ volatile("" ::: "memory");
+          const int rel = key - qlo - 4 * g;  // element j: query row offset 8 (j / 4) + j % 4
+#pragma unroll
+          for (int j = 0; j < 16; ++j) s[j] = ((j >> 2) * 8 + (j & 3) >= rel) ? s[j] : NEG_INF_F;
+        }
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          const float4 l4 = *reinterpret_cast<const float4*>(&LD[buf][jq * 8 + g * 4]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&LD[buf][BQ + jq * 8 + g * 4]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+          // rows 8 jq + 4 g + e, e = 0..3: (lse2, D) pairs
+          const float4 a = *reinterpret_cast<const float4*>(&LD[buf][2 * (jq * 8 + g * 4)]);
+          const float4 b = *reinterpret_cast<const float4*>(&LD[buf][2 * (jq * 8 + g * 4) + 4]);
+          const float lv[4] = {a.x, a.z, b.x, b.z};
+          const float dd[4] = {a.y, a.w, b.y, b.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * jq + e;
-            float pv = fast_exp2(fmaf(s[j], c, -lv[e] * LOG2E_F));
-            if (need_mask) pv = (key <= qlo + jq * 8 + g * 4 + e) ? pv : 0.f;
+            const float pv = fast_exp2(fmaf(s[j], c, -lv[e]));
             s[j] = pv;                     // P
             dp[j] = pv * (dp[j] - dd[e]);  // dS, in place
           }
@@ -439,20 +465,19 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
   if (tl > 0) {
     const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
     float* dq_acc = (float*)workspace;
-    float* dvec = (float*)((char*)workspace + o_al);
+    float* ldv = (float*)((char*)workspace + o_al);
     const int32_t* rowflags = m->d_tab + m->lay.rowflags;
     timing_begin(st, "bwd_pre");
     hipLaunchKernelGGL(bwd_pre_kernel, dim3(grid_for((long long)tl * hq * (d / 8), 256)), dim3(256), 0, st,
-                       (const uint16_t*)dout, (const uint16_t*)out, rowflags, dvec, tl, hq, d);
+                       (const uint16_t*)dout, (const uint16_t*)out, lse, (long long)m->t_alloc, rowflags, ldv, tl,
+                       hq, d);
     timing_end(st);
     if ((rc = hip_check(hipGetLastError(), "bwd_pre launch")) != CP_ATTN_OK) return rc;
     BwdParams base{};
     base.q = (const uint16_t*)q;
     base.dout = (const uint16_t*)dout;
-    base.lse = lse;
-    base.ld_lse = m->t_alloc;
-    base.dvec = dvec;
-    base.ld_d = tl;
+    base.ldv = ldv;
+    base.ld_ldv = tl;
     base.slot = m->d_tab + m->lay.cupl;
     base.hq = hq;
     base.hkv = hkv;

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 #include "kern_common.h"
@@ -52,8 +53,10 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][tile_bytes<D, false, BN>() / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][tile_bytes<D, true, BN>() / 2];
+  using KCopy = TileCopy<D, false, BN, NWAVES>;
+  using VCopy = TileCopy<D, true, BN, NWAVES>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][KCopy::BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][VCopy::BYTES / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -87,17 +90,82 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   float m_run = NEG_INF_F, l_run = 0.f;
 
   const int ldb = (int)(p.ld_kv * 2);
-  const long long range_bytes = (long long)kl * ldb;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)kvs * p.ld_kv + kvh * D, range_bytes);
+  const long long kv_end = (long long)kl * ldb;
+  const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
+  const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
+  KCopy kc;
+  VCopy vc;
+  kc.init(ldb, w, lane);
+  vc.init(ldb, w, lane);
   auto issue = [&](int kt, int buf) {
-    load_tile_lds<D, false, BN, NWAVES>(krs, Ks[buf], kt * BN * ldb, ldb, w, lane);
-    load_tile_lds<D, true, BN, NWAVES>(vrs, Vs[buf], kt * BN * ldb, ldb, w, lane);
+    const long long off = (long long)kt * BN * ldb;
+    kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
+    vc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
+  };
+
+  const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
+  // one key tile; masking runs only on a wavefront's last tiles (keys past
+  // the range, or at the causal step keys after its first row)
+  auto key_tile = [&](int kt, int buf, bool masked) {
+    const int k0 = kt * BN;
+    f32x16_t s[2];
+    s[0] = zero16();
+    s[1] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
+    }
+    if (masked) {
+      // a real branch (kept out of if-conversion), taken on few tiles
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
+          const bool ok = key < kl && (!p.causal || key <= qrow);
+          s[mb][j] = ok ? s[mb][j] : NEG_INF_F;
+        }
+    }
+    float mx = NEG_INF_F;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > m_run + lazy_thr;
+    if (__any(need)) {
+      const float alpha = need ? fast_exp2((m_run - mx) * c) : 1.f;
+      if (need) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[md][j] *= alpha;
+    }
+    const float base = (m_run == NEG_INF_F) ? 0.f : m_run * c;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = fast_exp2(fmaf(s[mb][j], c, -base));
+        s[mb][j] = pv;
+        lsum += pv;
+      }
+    l_run += lsum;
+#pragma unroll
+    for (int kk2 = 0; kk2 < 4; ++kk2) {
+      const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+        o[md] = mfma32x32x16(lds_read_tr<D, true>(Vs[buf], kk2 * 16, md * 32, lane), pb, o[md]);
+    }
   };
 
   if (nt > 0) issue(0, 0);
-
-  const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
@@ -106,62 +174,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
     const int k0 = kt * BN;
     const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
-    if (active) {
-      f32x16_t s[2];
-      s[0] = zero16();
-      s[1] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
-      }
-      const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
-      if (need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
-            const bool ok = key < kl && (!p.causal || key <= qrow);
-            s[mb][j] = ok ? s[mb][j] : NEG_INF_F;
-          }
-      }
-      float mx = NEG_INF_F;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = mx > m_run + lazy_thr;
-      if (__any(need)) {
-        const float alpha = need ? fast_exp2((m_run - mx) * c) : 1.f;
-        if (need) m_run = mx;
-        l_run *= alpha;
-#pragma unroll
-        for (int md = 0; md < NMD; ++md)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[md][j] *= alpha;
-      }
-      const float base = (m_run == NEG_INF_F) ? 0.f : m_run * c;
-      float lsum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float pv = fast_exp2(fmaf(s[mb][j], c, -base));
-          s[mb][j] = pv;
-          lsum += pv;
-        }
-      l_run += lsum;
-#pragma unroll
-      for (int kk2 = 0; kk2 < 4; ++kk2) {
-        const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
-#pragma unroll
-        for (int md = 0; md < NMD; ++md)
-          o[md] = mfma32x32x16(lds_read_tr<D, true>(Vs[buf], kk2 * 16, md * 32, lane), pb, o[md]);
-      }
-    }
+    const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
+    if (active) key_tile(kt, buf, need_mask);
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
@@ -289,7 +303,7 @@ extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int
   const size_t l = ((tl * hq * sizeof(float)) + 255) & ~size_t(255);
   const size_t o_al = (o + 255) & ~size_t(255);
   if (pass == 0) return 2 * o_al + 2 * l;  // accumulator + step partial (out, lse)
-  return o_al + l;                         // dq accumulator + D = rowsum(dO * O)
+  return o_al + 2 * l;                     // dq accumulator + per-row (lse, D = rowsum(dO * O)) pairs
 }
 
 static cp_attn_status check_common(const cp_attn_meta* m, const void* q, const void* const* ks, const void* const* vs,

@@ -121,8 +121,6 @@ __device__ __forceinline__ void map_block(int bid, int nheads, int& item, int& h
 // arithmetic.
 template <int D, bool TR_ONLY>
 __host__ __device__ constexpr int tile_rowb() { return TR_ONLY ? (D == 128 ? 320 : 192) : (D == 128 ? 304 : 144); }
-template <int D, bool TR_ONLY, int ROWS>
-__host__ __device__ constexpr int tile_bytes() { return ROWS * tile_rowb<D, TR_ONLY>(); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -140,28 +138,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 
 constexpr int OOB_OFFSET = 0x7ffffff0;  // any offset past num_records reads zeros
 
-// Copy one tile of ROWS x D bf16 (global rows `ld_bytes` apart, starting at
-// byte `row0_off` of the resource) into a padded LDS tile. The
-// tile is filled as a linear run of 16-byte units in 1 KB chunks shared by
-// the block's NW wavefronts; a lane whose unit is row padding loads zeros,
-// lanes past the tile's end stay idle.
+// Copy plan of one tile of ROWS x D bf16 (global rows ld_bytes apart) into a
+// padded LDS tile. The tile is filled as a linear run of 16-byte units in
+// 1 KB chunks (64 lanes x 16 bytes) dealt round-robin to the block's NW
+// wavefronts; the LDS tile spans whole chunks (BYTES), so lanes past the last
+// row only fill spare bytes with zeros. A lane's global offset within a tile
+// depends on the lane alone and is computed once (row padding units get an
+// offset past any buffer's end and load zeros). Each copy takes a buffer
+// resource whose base is the tile's first row and whose size ends at the
+// range's end, so rows past the range load zeros.
 template <int D, bool TR_ONLY, int ROWS, int NW>
-__device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, int row0_off,
-                                              int ld_bytes, int wave, int lane) {
-  constexpr int SU = tile_rowb<D, TR_ONLY>() / 16;  // units per padded row
-  constexpr int UPR = D * 2 / 16;              // units per data row
-  constexpr int UNITS = ROWS * SU;
-  constexpr int CHUNKS = (UNITS + 63) / 64;
+struct TileCopy {
+  static constexpr int SU = tile_rowb<D, TR_ONLY>() / 16;  // units per padded row
+  static constexpr int UPR = D * 2 / 16;                   // units per data row
+  static constexpr int UNITS = ROWS * SU;
+  static constexpr int CHUNKS = (UNITS + 63) / 64;
+  static constexpr int PER_WAVE = (CHUNKS + NW - 1) / NW;
+  static constexpr int BYTES = CHUNKS * 1024;
+  int voff[PER_WAVE];
+
+  __device__ __forceinline__ void init(int ld_bytes, int wave, int lane) {
 #pragma unroll
-  for (int cc = 0; cc < (CHUNKS + NW - 1) / NW; ++cc) {
-    const int c = cc * NW + wave;
-    const int u = c * 64 + lane;
-    if ((CHUNKS % NW == 0 || c < CHUNKS) && (UNITS % 64 == 0 || u < UNITS)) {
+    for (int cc = 0; cc < PER_WAVE; ++cc) {
+      const int u = (cc * NW + wave) * 64 + lane;
       const int row = u / SU, unit = u % SU;
-      const int off = unit < UPR ? row0_off + row * ld_bytes + unit * 16 : OOB_OFFSET;
-      load_lds16(rsrc, reinterpret_cast<char*>(lds_tile) + c * 1024, off);
+      voff[cc] = (unit < UPR && u < UNITS) ? row * ld_bytes + unit * 16 : OOB_OFFSET;
     }
   }
+  __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rsrc, void* lds_tile, int wave) const {
+#pragma unroll
+    for (int cc = 0; cc < PER_WAVE; ++cc) {
+      const int c = cc * NW + wave;
+      if (CHUNKS % NW == 0 || c < CHUNKS) load_lds16(rsrc, reinterpret_cast<char*>(lds_tile) + c * 1024, voff[cc]);
+    }
+  }
+};
+
+// Buffer resource over [base + off_bytes, base + end_bytes): rows from
+// off_bytes on, nothing once off_bytes passes end_bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const void* base, long long off_bytes, long long end_bytes) {
+  const long long n = end_bytes - off_bytes;
+  return make_rsrc(reinterpret_cast<const char*>(base) + off_bytes, n > 0 ? n : 0);
 }
 
 // b128 read of 16-byte unit `unit` of `row` (tiles with row reads).
