@@ -26,6 +26,38 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counters scaled by a plain copy's readings; a file under profiles/ holds the
+# figure with the SHA-256 of the kernel sources it was taken on, and the
+# figure is dropped once those sources change
+TRAFFIC_SOURCES = ("context_packed_attention_amd/csrc/bwd.hip", "context_packed_attention_amd/csrc/fwd.hip",
+                   "context_packed_attention_amd/csrc/kern_common.h", "context_packed_attention_amd/csrc/internal.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when there is none or the sources changed."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel sources sha256: `([0-9a-f]{64})`", text)
+    row = re.search(r"^\| " + re.escape(kernel) + r" \|[^\n]*\| ([0-9]+) \|\s*$", text, re.M)
+    if not sha or not row or sha.group(1) != kernel_sources_sha256():
+        return None
+    return int(row.group(1))
+
+
 # algorithmic flops per causal pair per query head, in units of head_dim
 ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_dkdv": 8, "bwd_dq": 2}
 EXEC_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_dkdv": 8, "bwd_dq": 6}
@@ -221,7 +253,8 @@ def main():
         per_launch = ALGO_FLOPS_PER_PAIR[dom] * d * hq * pairs * args.steps / dom_n
         achieved = per_launch / (dom_ms / dom_n * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dom, w["name"]),
                 "algo_flops_per_launch": per_launch, "avg_launch_ms": dom_ms / dom_n}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
