@@ -16,6 +16,10 @@
 #include "internal.h"
 #include "kern_common.h"
 
+#ifndef DKDV_DESC
+#define DKDV_DESC 1
+#endif
+
 namespace cpattn {
 
 struct BwdParams {
@@ -23,7 +27,8 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* ldv;   // per (head, local row): (lse * log2(e), D), fp32 pairs [hq, ld_ldv, 2]
+  const float* lse2;  // forward LSE in exp2 units, fp32 [hq, ld_ldv] (+inf on padding rows)
+  const float* negd;  // -D = -rowsum(dO * out), fp32 [hq, ld_ldv] (0 on padding rows)
   long long ld_ldv;
   const int32_t* q_start;
   const int32_t* q_len;
@@ -42,13 +47,13 @@ struct BwdParams {
 };
 
 // Per (head, local row): the forward's LSE in exp2 units and
-// D = rowsum(dO * out), as an fp32 pair [hq, t_local, 2]; padding rows get
-// (+inf, 0), so their probabilities vanish. 16 lanes cover one (row, head) of
-// D = 128 (8 lanes for D = 64).
+// -D = -rowsum(dO * out), as two fp32 planes [hq, t_local]; padding rows get
+// (+inf, 0), so their probabilities vanish. 16 lanes cover one (row, head)
+// of D = 128 (8 lanes for D = 64).
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ out,
                                                       const float* __restrict__ lse, long long ld_lse,
-                                                      const int32_t* __restrict__ rowflags, float* __restrict__ ldv,
-                                                      int t_local, int hq, int d) {
+                                                      const int32_t* __restrict__ rowflags, float* __restrict__ lse2,
+                                                      float* __restrict__ negd, int t_local, int hq, int d) {
   const int lanes = d / 8;
   const long long n = (long long)t_local * hq * lanes;
   for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
@@ -70,8 +75,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
     }
     for (int off = lanes >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (part == 0) {
-      const float l2 = valid ? lse[(long long)h * ld_lse + t] * LOG2E_F : __builtin_huge_valf();
-      *reinterpret_cast<float2*>(ldv + ((long long)h * t_local + t) * 2) = make_float2(l2, acc);
+      const long long i = (long long)h * t_local + t;
+      lse2[i] = valid ? lse[(long long)h * ld_lse + t] * LOG2E_F : __builtin_huge_valf();
+      negd[i] = -acc;
     }
   }
 }
@@ -115,9 +121,9 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
       df[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p.dout + roff + kk * 16) : make_uint4(0, 0, 0, 0));
     }
   }
-  const float2 ld = qok ? *reinterpret_cast<const float2*>(p.ldv + ((long long)head * p.ld_ldv + qs + qrow) * 2)
-                        : make_float2(__builtin_huge_valf(), 0.f);
-  const float lse2 = ld.x, dq_d = ld.y;
+  const long long li = (long long)head * p.ld_ldv + qs + qrow;
+  const float lse2 = qok ? p.lse2[li] : __builtin_huge_valf();
+  const float dq_d = qok ? -p.negd[li] : 0.f;
 
   f32x16_t acc[NMD];
 #pragma unroll
@@ -226,7 +232,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][QCopy::BYTES / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][QCopy::BYTES / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Vt[VCopy::BYTES / 2];  // the block's V rows
-  __shared__ __attribute__((aligned(16))) float LD[2][2 * BQ];  // per buffer: (lse * log2(e), D) per row
+  __shared__ __attribute__((aligned(16))) float LD[2][2 * BQ];  // per buffer: the rows' lse * log2(e), then -D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -270,34 +276,52 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
       vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, (long long)nk * ldkv), Vt, w);
     }
     const int ldb = (int)(p.ld_q * 2);
-    const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 8;
+    const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 4;
     QCopy qc;  // the same plan serves Q and dO
     qc.init(ldb, w, lane);
-    // query head hh, query tile qt: Q and dO rows, and the rows' (lse, D)
-    // pairs (256 bytes, copied by 16 lanes of wavefront 0)
+    // query head hh, query tile qt: Q and dO rows, and the rows' lse and -D
+    // (128 bytes each, copied by 16 lanes of wavefront 0)
     auto issue = [&](int hh, int qt, int buf) {
       const long long hoff = (long long)qs * p.ld_q + hh * D;
       const long long off = (long long)qt * BQ * ldb;
       qc.copy(rsrc_from(p.q + hoff, off, q_end), Qs[buf], w);
       qc.copy(rsrc_from(p.dout + hoff, off, q_end), Ds[buf], w);
       if (w == 0) {
-        const __amdgpu_buffer_rsrc_t lr =
-            rsrc_from(p.ldv + ((long long)hh * p.ld_ldv + qs) * 2, (long long)qt * BQ * 8, ld_end);
-        if (lane < BQ / 2) load_lds16(lr, &LD[buf][0], lane * 16);
+        const long long hrow = (long long)hh * p.ld_ldv + qs;
+        const long long toff = (long long)qt * BQ * 4;
+        const __amdgpu_buffer_rsrc_t lr = rsrc_from(p.lse2 + hrow, toff, ld_end);
+        const __amdgpu_buffer_rsrc_t dr = rsrc_from(p.negd + hrow, toff, ld_end);
+        if (lane < BQ / 4)
+          load_lds16(lr, &LD[buf][0], lane * 16);
+        else if (lane < BQ / 2)
+          load_lds16(dr, &LD[buf][0], (lane - BQ / 4) * 16);
       }
     };
-    static_assert(sizeof(LD[0]) == BQ * 8, "(lse, D) tile layout");
+    static_assert(sizeof(LD[0]) == BQ * 8, "lse / -D tile layout");
 
+#if DKDV_DESC
+    // query tiles last to first: every key block of a head starts on the same
+    // tile and the blocks move through the query rows together (shared L2)
+    int hh = kvh * p.group, qt = qt_end - 1;
+#else
     int hh = kvh * p.group, qt = qt_begin;
+#endif
     issue(hh, qt, 0);
     const int wkey_hi = k0 + w * 32 + 31;
     for (int it = 0; it < n_iter; ++it) {
       const int buf = it & 1;
       const int cur_qt = qt;
+#if DKDV_DESC
+      if (--qt < qt_begin) {
+        qt = qt_end - 1;
+        ++hh;
+      }
+#else
       if (++qt == qt_end) {
         qt = qt_begin;
         ++hh;
       }
+#endif
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (it + 1 < n_iter) issue(hh, qt, buf ^ 1);
@@ -306,8 +330,17 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
       // the future of a wavefront's keys are zeroed by the causal mask
       const int qlo = cur_qt * BQ;
       {
-        // S = Q K^T and dP = dO V^T: rows q (this lane: 16 of them), column key
-        f32x16_t s = zero16(), dp = zero16();
+        // S = Q K^T and dP - D = dO V^T - D: rows q (this lane: 16 of them),
+        // column key; the dP accumulator starts at -D of its rows
+        f32x16_t s = zero16(), dp;
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const float4 nd = *reinterpret_cast<const float4*>(&LD[buf][BQ + jq * 8 + g * 4]);
+          dp[4 * jq + 0] = nd.x;
+          dp[4 * jq + 1] = nd.y;
+          dp[4 * jq + 2] = nd.z;
+          dp[4 * jq + 3] = nd.w;
+        }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           s = mfma32x32x16(lds_read_row<D>(Qs[buf], l32, 2 * kk + g), kf[kk], s);
@@ -324,17 +357,15 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
         }
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          // rows 8 jq + 4 g + e, e = 0..3: (lse2, D) pairs
-          const float4 a = *reinterpret_cast<const float4*>(&LD[buf][2 * (jq * 8 + g * 4)]);
-          const float4 b = *reinterpret_cast<const float4*>(&LD[buf][2 * (jq * 8 + g * 4) + 4]);
-          const float lv[4] = {a.x, a.z, b.x, b.z};
-          const float dd[4] = {a.y, a.w, b.y, b.w};
+          // rows 8 jq + 4 g + e, e = 0..3
+          const float4 l4 = *reinterpret_cast<const float4*>(&LD[buf][jq * 8 + g * 4]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * jq + e;
             const float pv = fast_exp2(fmaf(s[j], c, -lv[e]));
-            s[j] = pv;                     // P
-            dp[j] = pv * (dp[j] - dd[e]);  // dS, in place
+            s[j] = pv;           // P
+            dp[j] = pv * dp[j];  // dS = P (dP - D), in place
           }
         }
         // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, two slices of 16)
@@ -464,19 +495,22 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
   cp_attn_status rc = CP_ATTN_OK;
   if (tl > 0) {
     const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
+    const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);
     float* dq_acc = (float*)workspace;
-    float* ldv = (float*)((char*)workspace + o_al);
+    float* lse2 = (float*)((char*)workspace + o_al);
+    float* negd = (float*)((char*)workspace + o_al + l_al);
     const int32_t* rowflags = m->d_tab + m->lay.rowflags;
     timing_begin(st, "bwd_pre");
     hipLaunchKernelGGL(bwd_pre_kernel, dim3(grid_for((long long)tl * hq * (d / 8), 256)), dim3(256), 0, st,
-                       (const uint16_t*)dout, (const uint16_t*)out, lse, (long long)m->t_alloc, rowflags, ldv, tl,
-                       hq, d);
+                       (const uint16_t*)dout, (const uint16_t*)out, lse, (long long)m->t_alloc, rowflags, lse2, negd,
+                       tl, hq, d);
     timing_end(st);
     if ((rc = hip_check(hipGetLastError(), "bwd_pre launch")) != CP_ATTN_OK) return rc;
     BwdParams base{};
     base.q = (const uint16_t*)q;
     base.dout = (const uint16_t*)dout;
-    base.ldv = ldv;
+    base.lse2 = lse2;
+    base.negd = negd;
     base.ld_ldv = tl;
     base.slot = m->d_tab + m->lay.cupl;
     base.hq = hq;

@@ -303,7 +303,7 @@ extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int
   const size_t l = ((tl * hq * sizeof(float)) + 255) & ~size_t(255);
   const size_t o_al = (o + 255) & ~size_t(255);
   if (pass == 0) return 2 * o_al + 2 * l;  // accumulator + step partial (out, lse)
-  return o_al + 2 * l;                     // dq accumulator + per-row (lse, D = rowsum(dO * O)) pairs
+  return o_al + 2 * l;                     // dq accumulator + per-row lse and -D = -rowsum(dO * O)
 }
 
 static cp_attn_status check_common(const cp_attn_meta* m, const void* q, const void* const* ks, const void* const* vs,
