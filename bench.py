@@ -4,7 +4,8 @@
 One step = the whole hot path over one batch: the per-rank metadata build,
 the forward (one flash kernel per ring step + LSE merges) and the backward
 (D preprocess, per-step dK/dV and dQ kernels, dQ finalize, tail zeroing when a
-tail exists). Inputs are seeded synthetic bf16 tensors already resident in
+tail exists). Beside it, the forward + backward captured once as a HIP graph is
+timed against the same calls made eagerly (the "graph" object). Inputs are seeded synthetic bf16 tensors already resident in
 HBM. The reported value is algorithmic TFLOP/s: 14 * D * Hq * causal pairs of
 the share per step (4 forward + 10 backward), divided by the measured time.
 
@@ -260,6 +261,35 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None}
 
+    # the share as one HIP graph launch: metadata built once per batch, then
+    # the captured forward + backward replayed; eager fwd + bwd (no timing
+    # events) timed beside it on the same buffers
+    gmeta = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+    graph = api.cp_attn_graph_capture(gmeta, 3, q, ks, vs, hq, hkv, d, scale, 1, out, lse, do, dq, dks, dvs,
+                                      ws_f, ws_b)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / n
+
+    def eager_fwd_bwd():
+        api.cp_attn_fwd(gmeta, q, ks, vs, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream)
+        api.cp_attn_bwd(gmeta, q, ks, vs, out, lse, do, hq, hkv, d, scale, 1, dq, dks, dvs, ws_b, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        graph.launch(stream)
+    eager_ms = timed(eager_fwd_bwd, args.steps)
+    graph_ms = timed(lambda: graph.launch(stream), args.steps)
+    graph_info = {"kernels_per_launch": graph.kernels, "eager_fwd_bwd_ms": round(eager_ms, 4),
+                  "graph_fwd_bwd_ms": round(graph_ms, 4), "saving_ms": round(eager_ms - graph_ms, 4)}
+    log(f"[bench] fwd+bwd eager {eager_ms:.3f} ms, one graph launch {graph_ms:.3f} ms ({graph.kernels} kernels)")
+    graph.close()
+    gmeta.close()
+
     cpu = None
     if args.cpu_sample_stride > 0:
         log("[bench] oracle CPU baseline")
@@ -287,6 +317,7 @@ def main():
         "metadata_call_ms": round(sorted(meta_ms)[len(meta_ms) // 2], 4),
         "kernels": kernels,
         "roofline": roof,
+        "graph": graph_info,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

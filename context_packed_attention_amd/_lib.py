@@ -22,6 +22,7 @@ EXPORTED = [
     "cp_attn_rank_metadata", "cp_attn_meta_summary", "cp_attn_meta_export", "cp_attn_meta_free",
     "cp_attn_workspace_bytes", "cp_attn_fwd", "cp_attn_bwd", "cp_attn_shard_gather", "cp_attn_last_error",
     "cp_attn_timing_enable", "cp_attn_timing_read",
+    "cp_attn_graph_capture", "cp_attn_graph_launch", "cp_attn_graph_kernels", "cp_attn_graph_free",
 ]
 
 
@@ -72,6 +73,15 @@ def load(path: str | None = None) -> C.CDLL:
     lib.cp_attn_timing_enable.restype = st
     lib.cp_attn_timing_read.argtypes = [C.c_char_p, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64), i32]
     lib.cp_attn_timing_read.restype = i32
+    lib.cp_attn_graph_capture.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, C.c_float, i32, vp, vp, vp, vp, vp,
+                                          vp, vp, C.c_size_t, vp, C.c_size_t, C.POINTER(vp)]
+    lib.cp_attn_graph_capture.restype = st
+    lib.cp_attn_graph_launch.argtypes = [vp, vp]
+    lib.cp_attn_graph_launch.restype = st
+    lib.cp_attn_graph_kernels.argtypes = [vp]
+    lib.cp_attn_graph_kernels.restype = C.c_int64
+    lib.cp_attn_graph_free.argtypes = [vp]
+    lib.cp_attn_graph_free.restype = None
     lib.cp_attn_last_error.argtypes = []
     lib.cp_attn_last_error.restype = C.c_char_p
     _lib = lib

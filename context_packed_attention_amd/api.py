@@ -212,3 +212,53 @@ def step_pairs(meta: Meta) -> list[int]:
         else:
             pairs.append(sum(a * b for a, b in zip(st["q_len"], st["kv_len"])))
     return pairs
+
+
+class Graph:
+    """Owns a cp_attn_graph: one rank share's forward and/or backward captured
+    as a HIP graph (freed on close / garbage collection). The tensors it was
+    captured with must outlive it; replays read their current contents."""
+
+    def __init__(self, handle: int, keep):
+        self._h = C.c_void_p(handle)
+        self._keep = keep  # the captured buffers stay referenced while the graph lives
+
+    @property
+    def kernels(self) -> int:
+        return int(L.load().cp_attn_graph_kernels(self._h))
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise ValueError("graph already freed")
+        _check(L.load().cp_attn_graph_launch(self._h, _stream(stream)), "cp_attn_graph_launch")
+
+    def close(self):
+        if self._h:
+            L.load().cp_attn_graph_free(self._h)
+            self._h = C.c_void_p(None)
+            self._keep = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def cp_attn_graph_capture(meta: Meta, passes: int, q, k_shards, v_shards, hq: int, hkv: int, d: int,
+                          softmax_scale: float, causal: int, out, lse, dout=None, dq=None, dk_parts=(),
+                          dv_parts=(), ws_fwd=None, ws_bwd=None) -> Graph:
+    ks = _ptr_array(k_shards)
+    vs = _ptr_array(v_shards)
+    dks = _ptr_array(dk_parts) if dk_parts else None
+    dvs = _ptr_array(dv_parts) if dv_parts else None
+    wf = ws_fwd.numel() * ws_fwd.element_size() if ws_fwd is not None else 0
+    wb = ws_bwd.numel() * ws_bwd.element_size() if ws_bwd is not None else 0
+    h = C.c_void_p()
+    rc = L.load().cp_attn_graph_capture(meta.handle, int(passes), _ptr(q), ks, vs, hq, hkv, d, float(softmax_scale),
+                                        int(causal), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), dks, dvs,
+                                        _ptr(ws_fwd), wf, _ptr(ws_bwd), wb, C.byref(h))
+    _check(rc, "cp_attn_graph_capture")
+    keep = (meta, q, tuple(k_shards), tuple(v_shards), out, lse, dout, dq, tuple(dk_parts), tuple(dv_parts),
+            ws_fwd, ws_bwd)
+    return Graph(h.value, keep)

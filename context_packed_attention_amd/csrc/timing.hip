@@ -39,15 +39,21 @@ void recycle_all() {
 }
 }  // namespace
 
+// launches being captured into a graph are not timed
+static bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
 void timing_begin(hipStream_t st, const char* name) {
-  if (!g_on) return;
+  if (!g_on || capturing(st)) return;
   Rec r{name, take_event(), take_event()};
   if (r.a) (void)hipEventRecord(r.a, st);
   g_recs.push_back(r);
 }
 
 void timing_end(hipStream_t st) {
-  if (!g_on || g_recs.empty()) return;
+  if (!g_on || g_recs.empty() || capturing(st)) return;
   Rec& r = g_recs.back();
   if (r.b) (void)hipEventRecord(r.b, st);
 }

@@ -195,11 +195,52 @@ cp_attn_status cp_attn_shard_gather(const cp_attn_meta* m, int32_t shard, const 
                                     void* local, size_t row_bytes, void* stream);
 
 /*
+ * One rank share as a single HIP graph launch. [I2] "Describe the bug"
+ * attributes the reference's lost time to gaps between many small launches
+ * on the main stream, and "Expected behavior" asks for padding metadata that
+ * stays valid under graph capture. The metadata is built once per batch
+ * (cp_attn_rank_metadata synchronises once and is not capturable); then the
+ * launches of cp_attn_fwd and/or cp_attn_bwd, with exactly these arguments,
+ * are captured on a private stream into an instantiated graph, and every
+ * cp_attn_graph_launch replays the whole share in one launch.
+ *
+ *  m, and the tensor / size / scale arguments: as cp_attn_fwd and cp_attn_bwd
+ *                     (dout, dq, dk_parts, dv_parts, ws_bwd are ignored when
+ *                     passes == 1; ws_fwd when passes == 2; lse and out are
+ *                     the forward's outputs and the backward's inputs)
+ *  passes             1 = forward, 2 = backward, 3 = forward then backward
+ *  out_graph          receives the library-owned graph handle
+ * The graph keeps the device pointers and sizes it was captured with (the
+ * host pointer arrays are read during capture only): every buffer must stay
+ * allocated, unmoved and of the same size while the graph is replayed, and
+ * `m` must not be freed before the graph. Each replay reads the inputs'
+ * contents at the time it runs. Errors found while capturing are returned as
+ * by cp_attn_fwd / cp_attn_bwd and leave no graph.
+ */
+typedef struct cp_attn_graph cp_attn_graph;
+
+cp_attn_status cp_attn_graph_capture(const cp_attn_meta* m, int32_t passes, const void* q,
+                                     const void* const* k_shards, const void* const* v_shards, int32_t hq,
+                                     int32_t hkv, int32_t d, float softmax_scale, int32_t causal, void* out,
+                                     float* lse, const void* dout, void* dq, void* const* dk_parts,
+                                     void* const* dv_parts, void* ws_fwd, size_t ws_fwd_bytes, void* ws_bwd,
+                                     size_t ws_bwd_bytes, cp_attn_graph** out_graph);
+
+/* Replay the captured share on `stream` (one graph launch; never synchronises). */
+cp_attn_status cp_attn_graph_launch(const cp_attn_graph* g, void* stream);
+
+/* Number of kernel launches the graph holds (host, no device work). */
+int64_t cp_attn_graph_kernels(const cp_attn_graph* g);
+
+/* Release the graph (waits for the device to finish its replays). NULL is a no-op. */
+void cp_attn_graph_free(cp_attn_graph* g);
+
+/*
  * Kernel timing (measurement tooling, not on the numerical path). While
  * enabled, every kernel launched by cp_attn_fwd / cp_attn_bwd is bracketed by
  * a pair of HIP events recorded on its launch stream (so the timing includes
- * nothing but that stream's work between the two records). Do not enable it
- * while capturing a HIP graph. Not thread-safe; meant for one benchmarking
+ * nothing but that stream's work between the two records). Launches made
+ * while their stream is being captured into a graph are not recorded. Not thread-safe; meant for one benchmarking
  * thread.
  * cp_attn_timing_enable(1) clears earlier records and starts recording;
  * cp_attn_timing_enable(0) stops recording.

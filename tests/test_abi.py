@@ -46,3 +46,12 @@ def test_host_argument_checks_without_gpu():
                            None) == _lib.ERR_INVALID_ARG
     assert lib.cp_attn_workspace_bytes(None, 1, 1, 128, 0) == 0
     lib.cp_attn_meta_free(None)
+    g = C.c_void_p()
+    assert lib.cp_attn_graph_capture(None, 3, None, None, None, 1, 1, 128, 1.0, 1, None, None, None, None, None,
+                                     None, None, 0, None, 0, C.byref(g)) == _lib.ERR_INVALID_ARG
+    assert not g.value
+    assert lib.cp_attn_graph_capture(dummy, 3, None, None, None, 1, 1, 128, 1.0, 1, None, None, None, None, None,
+                                     None, None, 0, None, 0, None) == _lib.ERR_INVALID_ARG
+    assert lib.cp_attn_graph_launch(None, None) == _lib.ERR_INVALID_ARG
+    assert lib.cp_attn_graph_kernels(None) == 0
+    lib.cp_attn_graph_free(None)

@@ -1,0 +1,106 @@
+"""HIP-graph capture of a rank share (cp_attn_graph_*): the metadata is built
+once, the forward and backward launches are captured, and every replay must
+equal the eager calls bit for bit (the kernels are deterministic: no atomics,
+fixed reduction order). Replays are checked one by one with eager work and
+synchronisations between them, again after the inputs change in place, and
+the graph must hold exactly the eager launch sequence ("[PyTorch][Attention]
+THD P2P context-parallel regression ...", "Expected behavior": padding
+metadata that is safe under graph capture)."""
+import math
+
+import numpy as np
+import pytest
+
+from context_packed_attention_amd import api, synth
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _same(name, a, b):
+    import torch
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"{name} differs from the eager result"
+
+
+@pytest.mark.parametrize("cfg,rank,tail", [(2, 1, 0), (3, 0, 0), (1, 1, 37)])
+def test_graph_replays_match_eager(cfg, rank, tail):
+    import torch
+    bt, w = synth.make_workload(cfg)
+    cp = w["cp"]
+    H.log(f"[graph] cfg{cfg} rank {rank} tail {tail}")
+    db = H.DeviceBatch(bt)
+    meta, loc = H.local_inputs(db, cp, rank, tail=tail)
+    scale = 1.0 / math.sqrt(bt.d)
+    tl = loc["t_local"]
+
+    def eager():
+        torch.cuda.synchronize()
+        api.cp_attn_timing_enable(True)
+        out, lse = H.run_fwd(meta, loc, bt, scale)
+        dq, dks, dvs = H.run_bwd(meta, loc, bt, scale, out, lse)
+        torch.cuda.synchronize()
+        api.cp_attn_timing_enable(False)
+        n = sum(v[1] for v in api.cp_attn_timing_read().values())
+        return (out, lse, dq, dks, dvs), n
+
+    ref, n_eager = eager()
+    out = torch.full_like(ref[0], 3.0)
+    lse = torch.full_like(ref[1], 3.0)
+    dq = torch.full_like(ref[2], 3.0)
+    dks = [torch.full_like(x, 3.0) for x in ref[3]]
+    dvs = [torch.full_like(x, 3.0) for x in ref[4]]
+    wsf = torch.empty(api.cp_attn_workspace_bytes(meta, bt.hq, bt.hkv, bt.d, 0), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(api.cp_attn_workspace_bytes(meta, bt.hq, bt.hkv, bt.d, 1), dtype=torch.uint8, device="cuda")
+    g = api.cp_attn_graph_capture(meta, 3, loc["q"], loc["k"], loc["v"], bt.hq, bt.hkv, bt.d, scale, 1, out, lse,
+                                  loc["do"], dq, dks, dvs, wsf, wsb)
+    H.log(f"[graph] {g.kernels} kernels captured, {n_eager} eager launches")
+    assert g.kernels == n_eager
+
+    def check(r):
+        _same("out", out[:tl], r[0][:tl])
+        _same("lse", lse[:, :tl], r[1][:, :tl])
+        _same("dq", dq, r[2])
+        for s in range(cp):
+            _same(f"dk[{s}]", dks[s], r[3][s])
+            _same(f"dv[{s}]", dvs[s], r[4][s])
+
+    for rep in range(3):
+        for t in [out, lse, dq, *dks, *dvs]:
+            t.fill_(5.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        check(ref)
+        H.log(f"[graph] replay {rep} matches")
+    # the graph reads its inputs' current contents
+    loc["q"].mul_(0.5)
+    loc["do"].mul_(-1.0)
+    ref2, _ = eager()
+    g.launch()
+    torch.cuda.synchronize()
+    check(ref2)
+    assert not torch.equal(ref2[2].view(torch.int16), ref[2].view(torch.int16))
+    g.close()
+    meta.close()
+
+
+def test_graph_capture_rejects_bad_arguments():
+    import torch
+    bt, w = synth.make_workload(1)
+    db = H.DeviceBatch(bt)
+    meta, loc = H.local_inputs(db, 2, 0)
+    out = torch.empty((loc["t_alloc"], bt.hq, bt.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((bt.hq, loc["t_alloc"]), dtype=torch.float32, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(api.CpAttnError) as e:
+        api.cp_attn_graph_capture(meta, 1, loc["q"], loc["k"], loc["v"], bt.hq, bt.hkv, bt.d, 0.125, 1, out, lse,
+                                  ws_fwd=small)
+    assert e.value.status == 4  # workspace too small, found while capturing; no graph is left
+    with pytest.raises(api.CpAttnError):
+        api.cp_attn_graph_capture(meta, 4, loc["q"], loc["k"], loc["v"], bt.hq, bt.hkv, bt.d, 0.125, 1, out, lse)
+    # the device still works after a failed capture
+    o2, l2 = H.run_fwd(meta, loc, bt, 0.125)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    meta.close()
