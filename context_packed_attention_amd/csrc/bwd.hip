@@ -213,18 +213,22 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 }
 
 // dK/dV of one ring step for the source shard's key rows. Block = NWAVES
-// wavefronts x 32 key rows of one KV head (DKDV_BN keys), K in
-// registers and V in LDS; loops over the query heads of the group and the step's query rows
-// in tiles of 32. Q and dO tiles are copied straight into padded LDS tiles
-// (double-buffered) together with the rows' LSE and D. Row-major reads feed
-// S = Q K^T and dP = dO V^T (lane = one key column); transposing reads feed
-// dV^T += dO^T P and dK^T += Q^T dS (lane = one key row of the output).
-// Query rows past the step's range read as zeros (Q = dO = D = 0), which
-// makes their dS and P.dO contributions vanish; key rows past the key range
-// are computed but written as zeros. Rows of the part outside the step's key
-// range are written as zeros too, so the whole shard-s part is defined.
+// wavefronts x DKDV_KB blocks of 32 key rows of one KV head (DKDV_BN keys),
+// K in registers and V in LDS; loops over the query heads of the group and
+// the step's query rows in tiles of 32. Q and dO tiles are copied straight
+// into padded LDS tiles (double-buffered) together with the rows' LSE and -D.
+// Row-major reads feed S = Q K^T and dP = dO V^T (lane = one key column);
+// transposing reads feed dV^T += dO^T P and dK^T += Q^T dS (lane = one key row
+// of the output). Each Q / dO fragment read from LDS serves all of a
+// wavefront's key blocks. Query rows past the step's range read as zeros
+// (Q = dO = D = 0), which makes their dS and P.dO contributions vanish; key
+// rows past the key range are computed but written as zeros. Rows of the part
+// outside the step's key range are written as zeros too, so the whole
+// shard-s part is defined.
 template <int D>
-__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 / NWAVES / DKDV_KB : 1)
+    bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KB = DKDV_KB;
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
   using QCopy = TileCopy<D, false, BQ, NWAVES>;
@@ -245,15 +249,17 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
   const int k0 = tile * BK;
   const int rows_here = min(BK, slot_len - k0);
   const int nk = max(0, min(BK, kl - k0));
-  const int key = k0 + w * 32 + l32;  // this lane's key row (relative to the slot)
+  const int wr0 = w * 32 * KB;  // the wavefront's first key row within the block
   const float c = p.c_log2;
 
-  f32x16_t dk[NMD], dv[NMD];
+  f32x16_t dk[KB][NMD], dv[KB][NMD];
 #pragma unroll
-  for (int md = 0; md < NMD; ++md) {
-    dk[md] = zero16();
-    dv[md] = zero16();
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) {
+      dk[kb][md] = zero16();
+      dv[kb][md] = zero16();
+    }
 
   // query tiles to visit: causal steps skip tiles entirely before this key tile
   const int qt_begin = (p.causal && nk > 0) ? (k0 / BQ) : 0;
@@ -262,14 +268,18 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
   const int n_iter = n_qt * p.group;
 
   if (n_iter > 0) {
-    // K rows of this lane's key in registers, the block's V rows in LDS
-    bf16x8_t kf[NKK];
-    {
+    // K rows of this lane's keys in registers, the block's V rows in LDS
+    bf16x8_t kf[KB][NKK];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key = k0 + wr0 + kb * 32 + l32;
       const bool ok = key < kl;
       const long long off = (long long)(kvs + (ok ? key : 0)) * p.ld_kv + kvh * D + g * 8;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.k + off + kk * 16) : make_uint4(0, 0, 0, 0));
+        kf[kb][kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.k + off + kk * 16) : make_uint4(0, 0, 0, 0));
+    }
+    {
       const int ldkv = (int)(p.ld_kv * 2);
       VCopy vcp;
       vcp.init(ldkv, w, lane);
@@ -307,7 +317,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
     int hh = kvh * p.group, qt = qt_begin;
 #endif
     issue(hh, qt, 0);
-    const int wkey_hi = k0 + w * 32 + 31;
+    const int wkey_hi = k0 + wr0 + 32 * KB - 1;
     for (int it = 0; it < n_iter; ++it) {
       const int buf = it & 1;
       const int cur_qt = qt;
@@ -331,29 +341,41 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
       const int qlo = cur_qt * BQ;
       {
         // S = Q K^T and dP - D = dO V^T - D: rows q (this lane: 16 of them),
-        // column key; the dP accumulator starts at -D of its rows
-        f32x16_t s = zero16(), dp;
+        // column key; the dP accumulators start at -D of their rows
+        f32x16_t s[KB], dp[KB];
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const float4 nd = *reinterpret_cast<const float4*>(&LD[buf][BQ + jq * 8 + g * 4]);
-          dp[4 * jq + 0] = nd.x;
-          dp[4 * jq + 1] = nd.y;
-          dp[4 * jq + 2] = nd.z;
-          dp[4 * jq + 3] = nd.w;
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = zero16();
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const float4 nd = *reinterpret_cast<const float4*>(&LD[buf][BQ + jq * 8 + g * 4]);
+            dp[kb][4 * jq + 0] = nd.x;
+            dp[kb][4 * jq + 1] = nd.y;
+            dp[kb][4 * jq + 2] = nd.z;
+            dp[kb][4 * jq + 3] = nd.w;
+          }
         }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s = mfma32x32x16(lds_read_row<D>(Qs[buf], l32, 2 * kk + g), kf[kk], s);
-          dp = mfma32x32x16(lds_read_row<D>(Ds[buf], l32, 2 * kk + g),
-                            lds_read_row<D>(Vt, w * 32 + l32, 2 * kk + g), dp);
+          const bf16x8_t qa = lds_read_row<D>(Qs[buf], l32, 2 * kk + g);
+          const bf16x8_t da = lds_read_row<D>(Ds[buf], l32, 2 * kk + g);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            s[kb] = mfma32x32x16(qa, kf[kb][kk], s[kb]);
+            dp[kb] = mfma32x32x16(da, lds_read_row<D>(Vt, wr0 + kb * 32 + l32, 2 * kk + g), dp[kb]);
+          }
         }
         if (p.causal && qlo < wkey_hi) {
-          // query rows before this lane's key (a real branch, kept out of
+          // query rows before a lane's key (a real branch, kept out of
           // if-conversion; only a wavefront's first tiles take it)
           __asm__ volatile("" ::: "memory");
-          const int rel = key - qlo - 4 * g;  // element j: query row offset 8 (j / 4) + j % 4
 #pragma unroll
-          for (int j = 0; j < 16; ++j) s[j] = ((j >> 2) * 8 + (j & 3) >= rel) ? s[j] : NEG_INF_F;
+          for (int kb = 0; kb < KB; ++kb) {
+            // element j: query row offset 8 (j / 4) + j % 4 from qlo + 4 g
+            const int rel = k0 + wr0 + kb * 32 + l32 - qlo - 4 * g;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[kb][j] = ((j >> 2) * 8 + (j & 3) >= rel) ? s[kb][j] : NEG_INF_F;
+          }
         }
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
@@ -361,49 +383,65 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dkdv_kernel(Bwd
           const float4 l4 = *reinterpret_cast<const float4*>(&LD[buf][jq * 8 + g * 4]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 4 * jq + e;
-            const float pv = fast_exp2(fmaf(s[j], c, -lv[e]));
-            s[j] = pv;           // P
-            dp[j] = pv * dp[j];  // dS = P (dP - D), in place
-          }
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = 4 * jq + e;
+              const float pv = fast_exp2(fmaf(s[kb][j], c, -lv[e]));
+              s[kb][j] = pv;               // P
+              dp[kb][j] = pv * dp[kb][j];  // dS = P (dP - D), in place
+            }
         }
         // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, two slices of 16)
 #pragma unroll
         for (int kq = 0; kq < BQ / 16; ++kq) {
-          const bf16x8_t pb = pack8_bf16(s, 8 * kq);
-          const bf16x8_t db = pack8_bf16(dp, 8 * kq);
+          bf16x8_t pb[KB], db[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            pb[kb] = pack8_bf16(s[kb], 8 * kq);
+            db[kb] = pack8_bf16(dp[kb], 8 * kq);
+          }
 #pragma unroll
           for (int md = 0; md < NMD; ++md) {
-            dv[md] = mfma32x32x16(lds_read_tr<D, false>(Ds[buf], kq * 16, md * 32, lane), pb, dv[md]);
-            dk[md] = mfma32x32x16(lds_read_tr<D, false>(Qs[buf], kq * 16, md * 32, lane), db, dk[md]);
+            const bf16x8_t ta = lds_read_tr<D, false>(Ds[buf], kq * 16, md * 32, lane);
+            const bf16x8_t tq = lds_read_tr<D, false>(Qs[buf], kq * 16, md * 32, lane);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dv[kb][md] = mfma32x32x16(ta, pb[kb], dv[kb][md]);
+              dk[kb][md] = mfma32x32x16(tq, db[kb], dk[kb][md]);
+            }
           }
         }
       }
     }
   }
-  // write this lane's key row: d = 32 md + 8 (j / 4) + 4 g + (j % 4)
-  if (w * 32 + l32 < rows_here) {
-    const bool ok = key < kl;
-    uint16_t* dkr = p.dk + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
-    uint16_t* dvr = p.dv + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+  // write this lane's key rows: d = 32 md + 8 (j / 4) + 4 g + (j % 4)
 #pragma unroll
-    for (int md = 0; md < NMD; ++md)
+  for (int kb = 0; kb < KB; ++kb) {
+    const int r = wr0 + kb * 32 + l32;
+    if (r < rows_here) {
+      const int key = k0 + r;
+      const bool ok = key < kl;
+      uint16_t* dkr = p.dk + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+      uint16_t* dvr = p.dv + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        uint2 a, b;
-        if (ok) {
-          a.x = pack2_bf16(dk[md][4 * jj] * p.scale, dk[md][4 * jj + 1] * p.scale);
-          a.y = pack2_bf16(dk[md][4 * jj + 2] * p.scale, dk[md][4 * jj + 3] * p.scale);
-          b.x = pack2_bf16(dv[md][4 * jj], dv[md][4 * jj + 1]);
-          b.y = pack2_bf16(dv[md][4 * jj + 2], dv[md][4 * jj + 3]);
-        } else {
-          a = make_uint2(0, 0);
-          b = make_uint2(0, 0);
+      for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint2 a, b;
+          if (ok) {
+            a.x = pack2_bf16(dk[kb][md][4 * jj] * p.scale, dk[kb][md][4 * jj + 1] * p.scale);
+            a.y = pack2_bf16(dk[kb][md][4 * jj + 2] * p.scale, dk[kb][md][4 * jj + 3] * p.scale);
+            b.x = pack2_bf16(dv[kb][md][4 * jj], dv[kb][md][4 * jj + 1]);
+            b.y = pack2_bf16(dv[kb][md][4 * jj + 2], dv[kb][md][4 * jj + 3]);
+          } else {
+            a = make_uint2(0, 0);
+            b = make_uint2(0, 0);
+          }
+          *reinterpret_cast<uint2*>(dkr + md * 32 + jj * 8) = a;
+          *reinterpret_cast<uint2*>(dvr + md * 32 + jj * 8) = b;
         }
-        *reinterpret_cast<uint2*>(dkr + md * 32 + jj * 8) = a;
-        *reinterpret_cast<uint2*>(dvr + md * 32 + jj * 8) = b;
-      }
+    }
   }
 }
 

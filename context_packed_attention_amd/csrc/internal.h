@@ -21,7 +21,12 @@ constexpr int BLOCK_THREADS = 64 * NWAVES;
 // Query rows per forward / dQ work item.
 constexpr int FWD_BM = 32 * NWAVES;
 // Key rows per dK/dV work item.
-constexpr int DKDV_BN = 32 * NWAVES;
+#ifndef CPA_DKDV_KB
+#define CPA_DKDV_KB 1
+#endif
+// 32-key blocks per dK/dV wavefront; the dK/dV block covers DKDV_BN keys
+constexpr int DKDV_KB = CPA_DKDV_KB;
+constexpr int DKDV_BN = 32 * NWAVES * DKDV_KB;
 // Work lists up to this length are sorted heaviest-first on the device.
 constexpr int SORT_CAP = 4096;
 
