@@ -130,13 +130,13 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   for (int md = 0; md < NMD; ++md) acc[md] = zero16();
 
   const int ldb = (int)(p.ld_kv * 2);
-  const long long kv_end = (long long)kl * ldb;
+  const int kv_end = kl * ldb;
   const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
   const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
   KCopy kc;
   kc.init(ldb, w, lane);
   auto issue = [&](int kt, int buf) {
-    const long long off = (long long)kt * BN * ldb;
+    const int off = kt * BN * ldb;
     kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
     kc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
   };
@@ -283,24 +283,28 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
       const int ldkv = (int)(p.ld_kv * 2);
       VCopy vcp;
       vcp.init(ldkv, w, lane);
-      vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, (long long)nk * ldkv), Vt, w);
+      vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, nk * ldkv), Vt, w);
     }
     const int ldb = (int)(p.ld_q * 2);
-    const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 4;
+    const int q_end = ql * ldb, ld_end = ql * 4;
     QCopy qc;  // the same plan serves Q and dO
     qc.init(ldb, w, lane);
+    // the step's first query row, and the head-to-head strides in bytes
+    const char* q_base = reinterpret_cast<const char*>(p.q + (long long)qs * p.ld_q);
+    const char* do_base = reinterpret_cast<const char*>(p.dout + (long long)qs * p.ld_q);
+    const char* l_base = reinterpret_cast<const char*>(p.lse2 + qs);
+    const char* n_base = reinterpret_cast<const char*>(p.negd + qs);
+    const int ld_head = (int)(p.ld_ldv * 4);
     // query head hh, query tile qt: Q and dO rows, and the rows' lse and -D
     // (128 bytes each, copied by 16 lanes of wavefront 0)
     auto issue = [&](int hh, int qt, int buf) {
-      const long long hoff = (long long)qs * p.ld_q + hh * D;
-      const long long off = (long long)qt * BQ * ldb;
-      qc.copy(rsrc_from(p.q + hoff, off, q_end), Qs[buf], w);
-      qc.copy(rsrc_from(p.dout + hoff, off, q_end), Ds[buf], w);
+      const int off = qt * (BQ * ldb);
+      qc.copy(rsrc_from(q_base + hh * (D * 2), off, q_end), Qs[buf], w);
+      qc.copy(rsrc_from(do_base + hh * (D * 2), off, q_end), Ds[buf], w);
       if (w == 0) {
-        const long long hrow = (long long)hh * p.ld_ldv + qs;
-        const long long toff = (long long)qt * BQ * 4;
-        const __amdgpu_buffer_rsrc_t lr = rsrc_from(p.lse2 + hrow, toff, ld_end);
-        const __amdgpu_buffer_rsrc_t dr = rsrc_from(p.negd + hrow, toff, ld_end);
+        const int toff = qt * (BQ * 4);
+        const __amdgpu_buffer_rsrc_t lr = rsrc_from(l_base + hh * ld_head, toff, ld_end);
+        const __amdgpu_buffer_rsrc_t dr = rsrc_from(n_base + hh * ld_head, toff, ld_end);
         if (lane < BQ / 4)
           load_lds16(lr, &LD[buf][0], lane * 16);
         else if (lane < BQ / 2)

@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   float m_run = NEG_INF_F, l_run = 0.f;
 
   const int ldb = (int)(p.ld_kv * 2);
-  const long long kv_end = (long long)kl * ldb;
+  const int kv_end = kl * ldb;
   const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
   const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
   KCopy kc;
@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   kc.init(ldb, w, lane);
   vc.init(ldb, w, lane);
   auto issue = [&](int kt, int buf) {
-    const long long off = (long long)kt * BN * ldb;
+    const int off = kt * BN * ldb;
     kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
     vc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
   };

@@ -175,9 +175,11 @@ struct TileCopy {
 };
 
 // Buffer resource over [base + off_bytes, base + end_bytes): rows from
-// off_bytes on, nothing once off_bytes passes end_bytes.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const void* base, long long off_bytes, long long end_bytes) {
-  const long long n = end_bytes - off_bytes;
+// off_bytes on, nothing once off_bytes passes end_bytes. Offsets are 32-bit
+// (the host keeps every tensor a kernel addresses this way below 2 GiB), so
+// the arithmetic stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const void* base, int off_bytes, int end_bytes) {
+  const int n = end_bytes - off_bytes;
   return make_rsrc(reinterpret_cast<const char*>(base) + off_bytes, n > 0 ? n : 0);
 }
 
