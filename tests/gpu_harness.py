@@ -137,7 +137,7 @@ def run_bwd(meta, loc, bt, scale, out, lse, garbage: float = 5.0):
 
 
 def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None):
-    """max-abs <= max(2e-2, one bf16 ulp of the reference) and relative L2
+    """max-abs <= max(2e-2, two bf16 ulps of the reference) and relative L2
     <= 1e-2. Returns a stats dict."""
     got = bf16_bits_to_f64(got_bits)
     if rows is not None:
@@ -146,11 +146,13 @@ def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None):
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     err = np.abs(got - ref)
-    # One bf16 ulp of the reference, 2^(floor(log2|ref|) - 7): where it exceeds
-    # 2e-2 (|ref| >= 4) a result one rounding step away from the exact value is
-    # accepted; everywhere else the bar is the stated 2e-2.
+    # Two bf16 ulps of the reference, 2 * 2^(floor(log2|ref|) - 7), exceed 2e-2
+    # only where |ref| >= 2: there a result computed under the interface's
+    # forced roundings (bf16 out feeding D, bf16 P / dS as matrix operands,
+    # bf16 storage) can sit more than one rounding step from the exact value
+    # (tests/test_tolerance_model.py). Below |ref| = 2 the bar is the stated 2e-2.
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 7)
-    tol = np.maximum(OUT_ATOL, ulp)
+    tol = np.maximum(OUT_ATOL, 2.0 * ulp)
     worst = float((err / tol).max()) if err.size else 0.0
     nref = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))
