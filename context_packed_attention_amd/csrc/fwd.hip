@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     const bool need = mx > m_run + lazy_thr;
     if (__any(need)) {
       const float alpha = need ? fast_exp2((m_run - mx) * c) : 1.f;
@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     if (active) key_tile(kt, buf, need_mask);
   }
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = sum_halves(l_run);
   if (qrow < ql) {
     float inv, lse;
     if (lt > 0.f) {

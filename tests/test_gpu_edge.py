@@ -2,12 +2,16 @@
 backward (dQ, every dK/dV part), every rank: the largest ring (CP = 16), a
 CP = 8 ragged pack, a pack with no valid token at all (every output row is
 padding: out, dQ, dK, dV exactly 0 and LSE -inf), many one-token sequences,
-and a GQA group of 8 query heads per KV head. Tolerances as in the other
-parity tests (bf16 max-abs 2e-2 and relative L2 1e-2, LSE 1e-3 relative)."""
+a GQA group of 8 query heads per KV head, and (forward) scores spread over
+hundreds of nats (Q and K scaled by 16, exact in bf16: the online softmax's
+running max must be the true row max, or exp2 overflows). Tolerances as in the other
+parity tests (bf16 max-abs 2e-2 or two ulps, relative L2 1e-2; LSE 1e-3
+relative)."""
 import numpy as np
 import pytest
 
 from context_packed_attention_amd import synth
+from oracle import cp_attn_oracle as O
 from tests import test_gpu_bwd as TB
 from tests import test_gpu_fwd as TF
 
@@ -37,3 +41,17 @@ def test_edge_fwd_bwd(case):
     bt = synth.make_batch(name, 29, L, P, hq, hkv, d)
     TF._check_fwd(bt, cp, range(cp))
     TB._check_bwd(bt, cp, range(cp), tail=5)
+
+
+def test_large_scores_fwd():
+    """Forward only: the running max is a forward concern. (With the softmax
+    this close to one-hot, dS = P (dP - D) is a difference of nearly equal
+    numbers and D can only be formed from the bf16 out the backward
+    receives, so the backward's error there is set by that rounding, not by
+    the kernels.)"""
+    L, P = [900, 130], [904, 136]
+    bt = synth.make_batch("large-scores-cp2", 31, L, P, 4, 2, 128)
+    for name in ("q", "k"):
+        x = O.bf16_to_f64(getattr(bt, name)) * 16.0  # a power of two: exact in bf16
+        setattr(bt, name, synth.f32_to_bf16_bits(x.astype(np.float32)))
+    TF._check_fwd(bt, 2, range(2))
