@@ -17,6 +17,10 @@ What is computed is the plain definition, written out slowly in float64 numpy:
   standard zig-zag reading (the pages do not spell it out).
 * Causal softmax attention forward (out, natural-log LSE) and its exact
   gradient: not on the pages; the textbook definition.
+* The hierarchical (a2a + p2p) front end's all-to-all of one a2a group, as a
+  row / head permutation: page "Hybrid / Hierarchical Context Parallel Skill",
+  sections "Enablement" and "Implementation Map" (CP = a2a size x p2p size);
+  the rank numbering inside the group is a reading, stated where it is coded.
 
 Readings taken where the pages are silent (each is listed in the design notes):
 padding sits at the end of each sequence's padded slot; valid rows fill the
@@ -27,7 +31,9 @@ rank's query rows only.
 
 Parity is pinned by the "not gpu" tests: brute force over an explicit mask of
 the whole pack, torch's fp64 CPU attention routine (out and LSE) and autograd,
-central finite differences, closed forms and the all-ranks invariants.
+central finite differences, closed forms and the all-ranks invariants; the
+all-to-all by the identity "CP-level shards, then the group's all-to-all =
+the p2p-level shard, split by heads" and its inverse.
 """
 from __future__ import annotations
 
@@ -136,6 +142,72 @@ def valid_mask(cu, cup) -> np.ndarray:
 def gather_shard(x: np.ndarray, cu, cup, cp: int, s: int) -> np.ndarray:
     """Rows of a global packed array that rank s holds, in its local order."""
     return x[shard_rows(cu, cup, cp, s)]
+
+
+# ---------------------------------------------------------------------------
+# hierarchical (a2a + p2p) front end: the all-to-all of one a2a group
+# ---------------------------------------------------------------------------
+# Page "Hybrid / Hierarchical Context Parallel Skill", sections "Enablement"
+# and "Implementation Map": CP = a2a size x p2p size, sequence lengths divide
+# by 2*CP. Reading (the pages do not spell out the numbering): the a2a groups
+# are runs of consecutive CP ranks, CP rank c = p * A + a for p2p rank p and
+# a2a rank a. The group's CP chunks {pA .. pA+A-1} and their mirrors are then
+# exactly the p2p-level chunks p and 2P-1-p (a p2p-level chunk is A
+# consecutive CP-level chunks), and the all-to-all trades the sequence split
+# inside the group for a head split: a2a rank a' ends with heads
+# [a' H/A, (a'+1) H/A) of the p2p rank's rows.
+
+def _a2a_slots(cup, cp: int, a2a: int, p: int):
+    """(sequence start in CP-local rows, in p2p-local rows, CP chunk rows)."""
+    cup = np.asarray(cup, dtype=np.int64)
+    if cp % a2a:
+        raise OracleError("cp must be a multiple of the a2a size")
+    P = cp // a2a
+    if not 0 <= p < P:
+        raise OracleError("p2p rank out of range")
+    for b in range(cup.size - 1):
+        if (cup[b + 1] - cup[b]) % (2 * cp):
+            raise OracleError("padded lengths must divide by 2*CP")
+        yield int(cup[b]) // cp, int(cup[b]) // P, int(cup[b + 1] - cup[b]) // (2 * cp)
+
+
+def a2a_seq_to_head(xs, cup, cp: int, a2a: int, p: int):
+    """All-to-all of a2a group p. xs[a] holds the CP-local rows of CP rank
+    p*A + a, all heads, [>= T_local, H, ...]. Returns A arrays: entry a' holds
+    heads [a' H/A, (a'+1) H/A) of p2p rank p's local rows (per sequence, CP
+    chunks pA, .., pA+A-1 and then their mirrors 2CP-1-(pA+A-1), .., 2CP-1-pA),
+    [A * T_local, H/A, ...]."""
+    A = a2a
+    H = xs[0].shape[1]
+    if H % A:
+        raise OracleError("heads must divide by the a2a size")
+    T_local = int(np.asarray(cup)[-1]) // cp
+    rows = np.zeros((A * T_local,) + xs[0].shape[1:], dtype=xs[0].dtype)
+    for base_cp, base_p, c in _a2a_slots(cup, cp, A, p):
+        for j in range(A):
+            # first half: CP chunk pA + j = first chunk of CP rank pA + j
+            rows[base_p + j * c: base_p + (j + 1) * c] = xs[j][base_cp: base_cp + c]
+            # second half: CP chunk 2CP-1-(pA+A-1-j) = second chunk of CP rank pA + A-1-j
+            rows[base_p + (A + j) * c: base_p + (A + j + 1) * c] = xs[A - 1 - j][base_cp + c: base_cp + 2 * c]
+    hs = H // A
+    return [rows[:, a * hs:(a + 1) * hs].copy() for a in range(A)]
+
+
+def a2a_head_to_seq(ys, cup, cp: int, a2a: int, p: int):
+    """The inverse all-to-all (gradients back to the sequence split): ys[a']
+    holds heads a' of p2p rank p's local rows, [A * T_local, H/A, ...];
+    returns A arrays [T_local, H, ...], entry a = CP rank p*A + a."""
+    A = a2a
+    hs = ys[0].shape[1]
+    T_local = int(np.asarray(cup)[-1]) // cp
+    full = np.concatenate(ys, axis=1)  # [A T_local, H, ...], heads in a2a-rank order
+    xs = [np.zeros((T_local,) + full.shape[1:], dtype=full.dtype) for _ in range(A)]
+    for base_cp, base_p, c in _a2a_slots(cup, cp, A, p):
+        for j in range(A):
+            xs[j][base_cp: base_cp + c] = full[base_p + j * c: base_p + (j + 1) * c]
+            xs[A - 1 - j][base_cp + c: base_cp + 2 * c] = full[base_p + (A + j) * c: base_p + (A + j + 1) * c]
+    del hs
+    return xs
 
 
 # ---------------------------------------------------------------------------
