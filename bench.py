@@ -77,6 +77,9 @@ def parse():
                     help="1..5: tiny / 16K pack / padded 16K pack / 131072-token GQA / 64K hierarchical pack")
     ap.add_argument("--cpu-sample-stride", type=int, default=256,
                     help="oracle baseline: every Nth query row of the share (0 = skip the baseline)")
+    ap.add_argument("--a2a", action="store_true",
+                    help="only time the hierarchical front end's all-to-all (sequence split -> head split and back) "
+                         "on the 64K hierarchical pack, [a2a, p2p] = [2, 2], Q of 32 heads, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and exit "
                          "(the known-size reference for the HBM byte counters)")
@@ -139,6 +142,60 @@ def cpu_baseline(batch, w, rank, scale, stride):
             "seconds": dt}
 
 
+def a2a_bench(args):
+    """The all-to-all of one a2a group on the 64K hierarchical pack: 65536
+    padded tokens, CP = 4 as [a2a, p2p] = [2, 2], 32 heads of 128 bf16 (the
+    query tensor before the head split). HBM-bound: every byte is read once
+    and written once."""
+    import numpy as np
+    import torch
+    from context_packed_attention_amd import api, synth
+    w = synth.workload(5)
+    A, P = 2, 2
+    cp = A * P
+    L = w["lengths"]
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    heads, d = 2 * w["hq"], w["d"]
+    T = int(cu[-1])
+    tl = T // cp
+    dcu = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    m = api.cp_attn_rank_metadata(dcu, None, cp, 0, -1, tl)
+    ins = [torch.randn((tl, heads, d), device="cuda").to(torch.bfloat16) for _ in range(A)]
+    outs = [torch.empty((A * tl, heads // A, d), dtype=torch.bfloat16, device="cuda") for _ in range(A)]
+    backs = [torch.empty_like(x) for x in ins]
+    stream = torch.cuda.current_stream()
+    moved = 2 * A * tl * heads * d * 2  # bytes read + written per call
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    fwd_ms = timed(lambda: api.cp_attn_a2a_seq_to_head(m, A, 0, heads, d * 2, ins, outs, stream=stream))
+    inv_ms = timed(lambda: api.cp_attn_a2a_head_to_seq(m, A, 0, heads, d * 2, outs, backs, stream=stream))
+    ok = all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(ins, backs))
+    m.close()
+    gbs = moved / (fwd_ms * 1e-3) / 1e9
+    line = {
+        "metric": "hierarchical a2a permutation (sequence split -> head split), GB/s on 1 MI355X",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(fwd_ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (N(0,1) bf16)",
+        "config": {"workload": w["name"] + "-a2a", "cp_size": cp, "a2a_size": A, "p2p_size": P, "heads": heads,
+                   "head_dim": d, "t_local": tl, "bytes_per_call": moved},
+        "inverse": {"ms": round(inv_ms, 5), "GB/s": round(moved / (inv_ms * 1e-3) / 1e9, 1), "round_trip_exact": ok},
+        "roofline": {"kernel": "a2a_seq_to_head", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -157,6 +214,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
+        return
+    if args.a2a:
+        a2a_bench(args)
         return
     w = synth.workload(args.workload)
     rank = w["ranks"][-1] if args.workload != 1 else 0

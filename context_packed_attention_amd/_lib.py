@@ -23,6 +23,7 @@ EXPORTED = [
     "cp_attn_workspace_bytes", "cp_attn_fwd", "cp_attn_bwd", "cp_attn_shard_gather", "cp_attn_last_error",
     "cp_attn_timing_enable", "cp_attn_timing_read",
     "cp_attn_graph_capture", "cp_attn_graph_launch", "cp_attn_graph_kernels", "cp_attn_graph_free",
+    "cp_attn_a2a_seq_to_head", "cp_attn_a2a_head_to_seq",
 ]
 
 
@@ -82,6 +83,9 @@ def load(path: str | None = None) -> C.CDLL:
     lib.cp_attn_graph_kernels.restype = C.c_int64
     lib.cp_attn_graph_free.argtypes = [vp]
     lib.cp_attn_graph_free.restype = None
+    for f in (lib.cp_attn_a2a_seq_to_head, lib.cp_attn_a2a_head_to_seq):
+        f.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+        f.restype = st
     lib.cp_attn_last_error.argtypes = []
     lib.cp_attn_last_error.restype = C.c_char_p
     _lib = lib

@@ -262,3 +262,21 @@ def cp_attn_graph_capture(meta: Meta, passes: int, q, k_shards, v_shards, hq: in
     keep = (meta, q, tuple(k_shards), tuple(v_shards), out, lse, dout, dq, tuple(dk_parts), tuple(dv_parts),
             ws_fwd, ws_bwd)
     return Graph(h.value, keep)
+
+
+def cp_attn_a2a_seq_to_head(meta: Meta, a2a_size: int, p2p_rank: int, heads: int, head_bytes: int, ins, outs,
+                            stream=None):
+    """Group p2p_rank's all-to-all: ins[a] = CP rank p*A + a's local tensor
+    (all heads), outs[a'] = head group a' of p2p rank p's local rows."""
+    rc = L.load().cp_attn_a2a_seq_to_head(meta.handle, int(a2a_size), int(p2p_rank), int(heads), int(head_bytes),
+                                          _ptr_array(ins), _ptr_array(outs), _stream(stream))
+    _check(rc, "cp_attn_a2a_seq_to_head")
+
+
+def cp_attn_a2a_head_to_seq(meta: Meta, a2a_size: int, p2p_rank: int, heads: int, head_bytes: int, ins, outs,
+                            stream=None):
+    """The inverse all-to-all: ins[a'] = head group a' of p2p rank p's local
+    rows, outs[a] = CP rank p*A + a's local tensor (all heads)."""
+    rc = L.load().cp_attn_a2a_head_to_seq(meta.handle, int(a2a_size), int(p2p_rank), int(heads), int(head_bytes),
+                                          _ptr_array(ins), _ptr_array(outs), _stream(stream))
+    _check(rc, "cp_attn_a2a_head_to_seq")

@@ -195,6 +195,38 @@ cp_attn_status cp_attn_shard_gather(const cp_attn_meta* m, int32_t shard, const 
                                     void* local, size_t row_bytes, void* stream);
 
 /*
+ * The all-to-all of one a2a group of hierarchical (a2a + p2p) context
+ * parallelism, played on one device. [I3] "Enablement" and "Implementation
+ * Map": CP = a2a size x p2p size and every padded length divides by 2*CP;
+ * [I1]: THD with the a2a and hierarchical communication types is what the
+ * reference lacks. Reading: the a2a groups are runs of consecutive CP ranks
+ * (CP rank c = p * a2a_size + a), so group p's chunks are exactly p2p rank
+ * p's load-balanced chunk pair when each sequence is cut into 2 * (CP /
+ * a2a_size) chunks. The row mapping is the same for every group.
+ *
+ *  m           metadata built with cp_size = CP (any rank): its device tables
+ *              and its validation of the 2*CP divisibility are used
+ *  a2a_size    A, dividing CP; p2p_rank: the group p (< CP / A)
+ *  heads       heads per row (a multiple of A); head_bytes: bytes of one head
+ *              (head_dim * element size), a multiple of 16
+ * cp_attn_a2a_seq_to_head:
+ *  in          HOST array of A device pointers: entry a = CP rank p*A + a's
+ *              local tensor, [>= T_local, heads, head_bytes] (its layout per
+ *              the conventions above; rows >= T_local are not read)
+ *  out         HOST array of A device pointers: entry a' receives heads
+ *              [a' heads/A, (a'+1) heads/A) of p2p rank p's local rows,
+ *              [A * T_local, heads/A, head_bytes] (per sequence: CP chunks
+ *              pA .. pA+A-1, then their mirrors, 2CP-1-(pA+A-1) .. 2CP-1-pA)
+ * cp_attn_a2a_head_to_seq: the inverse (the gradients' way back), in/out
+ *              with the roles above swapped.
+ * T_local = cu_seqlens_padded[B] / CP. Never synchronises; capturable.
+ */
+cp_attn_status cp_attn_a2a_seq_to_head(const cp_attn_meta* m, int32_t a2a_size, int32_t p2p_rank, int32_t heads,
+                                       int32_t head_bytes, const void* const* in, void* const* out, void* stream);
+cp_attn_status cp_attn_a2a_head_to_seq(const cp_attn_meta* m, int32_t a2a_size, int32_t p2p_rank, int32_t heads,
+                                       int32_t head_bytes, const void* const* in, void* const* out, void* stream);
+
+/*
  * One rank share as a single HIP graph launch. [I2] "Describe the bug"
  * attributes the reference's lost time to gaps between many small launches
  * on the main stream, and "Expected behavior" asks for padding metadata that

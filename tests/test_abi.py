@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "cp_attn.h")
 def declared_symbols():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(cp_attn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(cp_attn_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
@@ -55,3 +55,5 @@ def test_host_argument_checks_without_gpu():
     assert lib.cp_attn_graph_launch(None, None) == _lib.ERR_INVALID_ARG
     assert lib.cp_attn_graph_kernels(None) == 0
     lib.cp_attn_graph_free(None)
+    assert lib.cp_attn_a2a_seq_to_head(None, 2, 0, 4, 256, None, None, None) == _lib.ERR_INVALID_ARG
+    assert lib.cp_attn_a2a_head_to_seq(None, 2, 0, 4, 256, None, None, None) == _lib.ERR_INVALID_ARG
