@@ -48,7 +48,7 @@ def load(path: str | None = None) -> C.CDLL:
         return _lib
     p = path or LIB_PATH
     if not os.path.exists(p):
-        raise RuntimeError(f"libcpattn.so not built ({p}); run __graft_entry__.build()")
+        raise RuntimeError(f"libcpattn.so not built ({p}); build it with python -m context_packed_attention_amd.build")
     lib = C.CDLL(p)
     vp = C.c_void_p
     i32 = C.c_int32
