@@ -130,13 +130,13 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   for (int md = 0; md < NMD; ++md) acc[md] = zero16();
 
   const int ldb = (int)(p.ld_kv * 2);
-  const int kv_end = kl * ldb;
+  const long long kv_end = (long long)kl * ldb;
   const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
   const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
   KCopy kc;
   kc.init(ldb, w, lane);
   auto issue = [&](int kt, int buf) {
-    const int off = kt * BN * ldb;
+    const long long off = (long long)kt * BN * ldb;
     kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
     kc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
   };
@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 // rows past the key range are computed but written as zeros. Rows of the part
 // outside the step's key range are written as zeros too, so the whole
 // shard-s part is defined.
-template <int D>
+template <int D, bool BIG>
 __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 / NWAVES / DKDV_KB : 1)
     bwd_dkdv_kernel(BwdParams p) {
   constexpr int KB = DKDV_KB;
@@ -283,10 +283,10 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
       const int ldkv = (int)(p.ld_kv * 2);
       VCopy vcp;
       vcp.init(ldkv, w, lane);
-      vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, nk * ldkv), Vt, w);
+      vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, (long long)nk * ldkv), Vt, w);
     }
     const int ldb = (int)(p.ld_q * 2);
-    const int q_end = ql * ldb, ld_end = ql * 4;
+    const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 4;
     QCopy qc;  // the same plan serves Q and dO
     qc.init(ldb, w, lane);
     // the step's first query row, and the head-to-head strides in bytes
@@ -294,17 +294,25 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     const char* do_base = reinterpret_cast<const char*>(p.dout + (long long)qs * p.ld_q);
     const char* l_base = reinterpret_cast<const char*>(p.lse2 + qs);
     const char* n_base = reinterpret_cast<const char*>(p.negd + qs);
-    const int ld_head = (int)(p.ld_ldv * 4);
+    const long long ld_head = p.ld_ldv * 4;
     // query head hh, query tile qt: Q and dO rows, and the rows' lse and -D
     // (128 bytes each, copied by 16 lanes of wavefront 0)
+    // BIG: local query tensors of 2 GiB or more need 64-bit offsets; below
+    // that the cheaper 32-bit scalar arithmetic serves
     auto issue = [&](int hh, int qt, int buf) {
-      const int off = qt * (BQ * ldb);
-      qc.copy(rsrc_from(q_base + hh * (D * 2), off, q_end), Qs[buf], w);
-      qc.copy(rsrc_from(do_base + hh * (D * 2), off, q_end), Ds[buf], w);
+      if constexpr (BIG) {
+        const long long off = (long long)qt * (BQ * ldb);
+        qc.copy(rsrc_from(q_base + hh * (D * 2), off, q_end), Qs[buf], w);
+        qc.copy(rsrc_from(do_base + hh * (D * 2), off, q_end), Ds[buf], w);
+      } else {
+        const int off = qt * (BQ * ldb);
+        qc.copy(rsrc_from32(q_base + hh * (D * 2), off, (int)q_end), Qs[buf], w);
+        qc.copy(rsrc_from32(do_base + hh * (D * 2), off, (int)q_end), Ds[buf], w);
+      }
       if (w == 0) {
         const int toff = qt * (BQ * 4);
-        const __amdgpu_buffer_rsrc_t lr = rsrc_from(l_base + hh * ld_head, toff, ld_end);
-        const __amdgpu_buffer_rsrc_t dr = rsrc_from(n_base + hh * ld_head, toff, ld_end);
+        const __amdgpu_buffer_rsrc_t lr = rsrc_from32(l_base + hh * ld_head, toff, (int)ld_end);
+        const __amdgpu_buffer_rsrc_t dr = rsrc_from32(n_base + hh * ld_head, toff, (int)ld_end);
         if (lane < BQ / 4)
           load_lds16(lr, &LD[buf][0], lane * 16);
         else if (lane < BQ / 2)
@@ -572,8 +580,8 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != m->device)
     return fail(CP_ATTN_ERR_INVALID_ARG, "current device differs from the metadata's device");
-  if ((long long)m->t_alloc * hq * d * 2 >= (1ll << 31))
-    return fail(CP_ATTN_ERR_UNSUPPORTED, "local tensors must stay below 2 GiB (32-bit buffer offsets)");
+  if ((long long)hq * d * 2 > (1ll << 20))
+    return fail(CP_ATTN_ERR_UNSUPPORTED, "a row of all heads must stay within 1 MiB");
   hipStream_t st = (hipStream_t)stream;
   const int tl = m->sum.t_local;
   cp_attn_status rc = CP_ATTN_OK;
@@ -605,6 +613,7 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     base.scale = softmax_scale;
     base.c_log2 = softmax_scale * LOG2E_F;
     base.dq_acc = dq_acc;
+    const bool big = (long long)tl * hq * d * 2 >= (1ll << 31);  // local query tensors of 2 GiB or more
     // Short launches (every dQ launch under four full waves of blocks) leave
     // tails a concurrent chain can fill: then dK/dV runs on the side stream,
     // forked from the caller's; long launches stay on one stream (co-resident
@@ -639,10 +648,17 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
       if (nkv > 0) {
         p.items = m->d_tab + m->lay.dkdv_tiles + (int64_t)i * m->lay.dkdv_cap * 2;
         timing_begin(sk, "bwd_dkdv");
-        if (d == 128)
-          hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
-        else
-          hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
+        if (d == 128) {
+          if (big)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
+          else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
+        } else {
+          if (big)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
+          else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
+        }
         timing_end(sk);
         if ((lrc = hip_check(hipGetLastError(), "bwd_dkdv launch")) != CP_ATTN_OK) break;
       }

@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   float m_run = NEG_INF_F, l_run = 0.f;
 
   const int ldb = (int)(p.ld_kv * 2);
-  const int kv_end = kl * ldb;
+  const long long kv_end = (long long)kl * ldb;
   const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
   const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
   KCopy kc;
@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   kc.init(ldb, w, lane);
   vc.init(ldb, w, lane);
   auto issue = [&](int kt, int buf) {
-    const int off = kt * BN * ldb;
+    const long long off = (long long)kt * BN * ldb;
     kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
     vc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
   };
@@ -339,8 +339,8 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   if (((uintptr_t)workspace) & 255) return fail(CP_ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const int tl = m->sum.t_local;
   if (tl == 0) return CP_ATTN_OK;
-  if ((long long)m->t_alloc * hkv * d * 2 >= (1ll << 31))
-    return fail(CP_ATTN_ERR_UNSUPPORTED, "a K/V shard must stay below 2 GiB (32-bit buffer offsets)");
+  if ((long long)hq * d * 2 > (1ll << 20))
+    return fail(CP_ATTN_ERR_UNSUPPORTED, "a row of all heads must stay within 1 MiB");
   hipStream_t st = (hipStream_t)stream;
   const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
   const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);

@@ -187,12 +187,20 @@ struct TileCopy {
 };
 
 // Buffer resource over [base + off_bytes, base + end_bytes): rows from
-// off_bytes on, nothing once off_bytes passes end_bytes. Offsets are 32-bit
-// (the host keeps every tensor a kernel addresses this way below 2 GiB), so
-// the arithmetic stays in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const void* base, int off_bytes, int end_bytes) {
+// off_bytes on, nothing once off_bytes passes end_bytes. The base is rebased
+// on off_bytes in 64-bit arithmetic, so tensors of any size can be
+// addressed; the record count is capped at RSRC_CAP (far more than any tile
+// reads), which keeps OOB_OFFSET out of range.
+constexpr long long RSRC_CAP = 1ll << 30;
+// the same with 32-bit offsets, for ranges known to stay below 2 GiB
+// (cheaper scalar arithmetic on the per-iteration path)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from32(const void* base, int off_bytes, int end_bytes) {
   const int n = end_bytes - off_bytes;
   return make_rsrc(reinterpret_cast<const char*>(base) + off_bytes, n > 0 ? n : 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const void* base, long long off_bytes, long long end_bytes) {
+  const long long n = end_bytes - off_bytes;
+  return make_rsrc(reinterpret_cast<const char*>(base) + off_bytes, n <= 0 ? 0 : (n < RSRC_CAP ? n : RSRC_CAP));
 }
 
 // b128 read of 16-byte unit `unit` of `row` (tiles with row reads).

@@ -185,3 +185,13 @@ def make_workload(cfg: int) -> tuple[PackedBatch, dict]:
         padded = draw_padded_lengths(w["seed"], lengths, w["max_pad"], 2 * w["cp"])
     batch = make_batch(w["name"], w["seed"], lengths, padded, w["hq"], w["hkv"], w["d"])
     return batch, w
+
+
+def device_normal_bf16(shape, seed: int):
+    """Seeded N(0, 1) bf16 tensor drawn directly on the current GPU (for
+    shapes too large to draw and upload from the host); the same seed and
+    shape give the same tensor."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=g, device="cuda", dtype=torch.bfloat16)

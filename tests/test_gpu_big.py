@@ -1,0 +1,79 @@
+"""A share whose local tensors reach 2 GiB: one 262144-token sequence, CP = 2,
+rank 0, 64 query heads and 8 KV heads of 128 (the local Q, dO, out and dQ are
+2 GiB each, the forward workspace 8 GiB). The tile copies address every
+tensor through buffer resources rebased on each tile in 64-bit arithmetic.
+Inputs are drawn on the device from fixed seeds and copied to the host only
+where the oracle reads them: out / LSE / dQ on sampled rows, and exact dK / dV
+on the last key rows of the rank's own shard (only the sequence's last
+queries reach them)."""
+import math
+
+import numpy as np
+import pytest
+
+from context_packed_attention_amd import api, synth
+from oracle import cp_attn_oracle as O
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_share_past_2gib():
+    import torch
+    T, cp, r, hq, hkv, d = 262144, 2, 0, 64, 8, 128
+    tl = T // cp
+    scale = 1.0 / math.sqrt(d)
+    cu = np.array([0, T], dtype=np.int32)
+    H.log(f"[big] T={T} cp={cp} rank={r} hq={hq} hkv={hkv}: local Q {tl * hq * d * 2 / 2**30:.2f} GiB")
+    gq = synth.device_normal_bf16((T, hq, d), 51)
+    gk = synth.device_normal_bf16((T, hkv, d), 52)
+    gv = synth.device_normal_bf16((T, hkv, d), 53)
+    gdo = synth.device_normal_bf16((T, hq, d), 54)
+    meta = api.cp_attn_rank_metadata(H.dev_i32(cu), H.dev_i32(cu.copy()), cp, r, -1, tl)
+
+    def gather(src, h, s):
+        dst = torch.empty((tl, h, d), dtype=torch.bfloat16, device="cuda")
+        api.cp_attn_shard_gather(meta, s, src, dst, h * d * 2)
+        return dst
+
+    loc = {"q": gather(gq, hq, r), "do": gather(gdo, hq, r), "k": [gather(gk, hkv, s) for s in range(cp)],
+           "v": [gather(gv, hkv, s) for s in range(cp)], "t_alloc": tl, "t_local": tl}
+    # host copies of what the oracle reads: every key / value, and the query
+    # rows it evaluates
+    own = O.shard_rows(cu, cu, cp, r)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, tl // 2 - 1, tl // 2, tl - 2, tl - 1], rng.integers(0, tl, 8)]))
+    keys = np.arange(tl - 4, tl)                       # local rows of the rank's own shard
+    reach = np.arange(int(own[keys[0]]), T)            # global query positions at or after them
+    need = np.unique(np.concatenate([own[rows], reach]))
+    qh = np.zeros((T, hq, d), dtype=np.uint16)
+    doh = np.zeros((T, hq, d), dtype=np.uint16)
+    idx = torch.from_numpy(need).to("cuda")
+    qh[need] = _bits(gq.index_select(0, idx))
+    doh[need] = _bits(gdo.index_select(0, idx))
+    kh, vh = _bits(gk), _bits(gv)
+    del gq, gdo, gk, gv
+    torch.cuda.empty_cache()
+    H.log("[big] GPU fwd + bwd")
+    bt = synth.PackedBatch(name="big", seed=51, cu=cu, cup=cu.copy(), hq=hq, hkv=hkv, d=d, q=qh, k=kh, v=vh, do=doh)
+    out, lse = H.run_fwd(meta, loc, bt, scale)
+    dq, dks, dvs = H.run_bwd(meta, loc, bt, scale, out, lse)
+    torch.cuda.synchronize()
+    heads = [0, 17, 63]
+    H.log(f"[big] oracle: {rows.size} rows x {len(heads)} heads")
+    o, l, dqr = O.share_rows(qh, kh, vh, doh, cu, cu, cp, r, scale, rows, heads, want_dq=True)
+    ridx = torch.from_numpy(rows).to("cuda")
+    H.compare_bf16("out", _bits(out.index_select(0, ridx)[:, heads]), o)
+    H.compare_lse("lse", lse[heads][:, ridx].cpu().numpy(), l)
+    H.compare_bf16("dq", _bits(dq.index_select(0, ridx)[:, heads]), dqr)
+    H.log(f"[big] oracle: dK / dV of {keys.size} key rows")
+    dk, dv = O.share_keys_dkdv(qh, kh, vh, doh, cu, cu, cp, r, scale, r, keys, [0, hkv - 1])
+    kidx = torch.from_numpy(keys).to("cuda")
+    H.compare_bf16("dk", _bits(dks[r].index_select(0, kidx)[:, [0, hkv - 1]]), dk)
+    H.compare_bf16("dv", _bits(dvs[r].index_select(0, kidx)[:, [0, hkv - 1]]), dv)
+    meta.close()
