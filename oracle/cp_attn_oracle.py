@@ -406,6 +406,72 @@ def share(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: floa
     return outd
 
 
+BF16_UNIT_ROUNDOFF = 2.0 ** -8   # round-to-nearest-even, 8-bit significand
+
+
+def share_rounding_sd(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float):
+    """Tolerance model for comparing a bf16 implementation with this oracle
+    (not part of the method): the standard deviation, per element of rank r's
+    share, of the error that three roundings forced by the interface induce,
+    each taken as an independent unbiased relative error of variance u^2 / 3
+    (u = 2^-8, bf16):
+
+    * P enters the P V and P^T dO contractions as a bf16 matrix operand;
+    * dS = P (dP - D) enters dS K and dS^T Q as a bf16 operand;
+    * D = rowsum(dO * out) is formed from the output the backward receives,
+      which carries its own bf16 rounding and that of P in P V, so D_i
+      carries var_D = u^2/3 (sum_d dO_id^2 out_id^2 + sum_j P_ij^2 dP_ij^2);
+      it reaches dQ_i through -scale D_i sum_j P_ij K_j (one error per row)
+      and dK_j through -scale sum_i P_ij D_i Q_i (independent per row i).
+
+    Returns {"out", "dq": [T_local, Hq, D], "dk_parts", "dv_parts": lists of
+    [T_local, Hkv, D]} in rank r's / shard s's local layouts (0 where an
+    element is not computed).
+    """
+    cu, cup = validate(cu, cup, cp, r)
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_bits)
+    v = bf16_to_f64(v_bits)
+    do = bf16_to_f64(do_bits)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    c = BF16_UNIT_ROUNDOFF ** 2 / 3.0
+    rank_of, _ = owner_map(cu, cup, cp)
+    var_out = np.zeros((T, hq, d))
+    var_dq = np.zeros((T, hq, d))
+    var_dk = np.zeros((T, hkv, d))
+    var_dv = np.zeros((T, hkv, d))
+    for b in range(cu.size - 1):
+        base = int(cup[b])
+        Lb = int(cu[b + 1] - cu[b])
+        pos = np.nonzero(rank_of[base:base + Lb] == r)[0]
+        if pos.size == 0:
+            continue
+        for h in range(hq):
+            kvh = h // group
+            K, V = k[base:base + Lb, kvh], v[base:base + Lb, kvh]
+            Q, dO = q[base + pos, h], do[base + pos, h]
+            S = scale * (Q @ K.T)
+            S = np.where(np.arange(Lb)[None, :] <= pos[:, None], S, NEG_INF)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            out = P @ V
+            dP = dO @ V.T
+            dS = P * (dP - (dO * out).sum(axis=1, keepdims=True))
+            var_D = c * (((dO * out) ** 2).sum(axis=1) + ((P * dP) ** 2).sum(axis=1))
+            var_out[base + pos, h] = c * ((P ** 2) @ (V ** 2))
+            var_dq[base + pos, h] = c * scale ** 2 * ((dS ** 2) @ (K ** 2)) + \
+                scale ** 2 * var_D[:, None] * (P @ K) ** 2
+            var_dk[base:base + Lb, kvh] += c * scale ** 2 * ((dS ** 2).T @ (Q ** 2)) + \
+                scale ** 2 * (P ** 2).T @ (var_D[:, None] * Q ** 2)
+            var_dv[base:base + Lb, kvh] += c * ((P ** 2).T @ (dO ** 2))
+    own = shard_rows(cu, cup, cp, r)
+    return {"out": np.sqrt(var_out[own]), "dq": np.sqrt(var_dq[own]),
+            "dk_parts": [np.sqrt(var_dk[shard_rows(cu, cup, cp, s)]) for s in range(cp)],
+            "dv_parts": [np.sqrt(var_dv[shard_rows(cu, cup, cp, s)]) for s in range(cp)]}
+
+
 class _HeadCache:
     """float64 copies of one KV head's keys and values, converted on first use."""
 

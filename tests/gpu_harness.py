@@ -136,13 +136,17 @@ def run_bwd(meta, loc, bt, scale, out, lse, garbage: float = 5.0):
     return dq, dks, dvs
 
 
-def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None):
-    """max-abs <= max(2e-2, two bf16 ulps of the reference) and relative L2
-    <= 1e-2. Returns a stats dict."""
+def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None, sd=None):
+    """max-abs <= max(2e-2, two bf16 ulps of the reference, half an ulp + 6 sd)
+    and relative L2 <= 1e-2; sd (optional) is the oracle's per-element
+    standard deviation of the interface's forced roundings
+    (cp_attn_oracle.share_rounding_sd). Returns a stats dict."""
     got = bf16_bits_to_f64(got_bits)
     if rows is not None:
         got = got[rows]
         ref = ref[rows]
+        if sd is not None:
+            sd = sd[rows]
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     err = np.abs(got - ref)
@@ -151,8 +155,13 @@ def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None):
     # forced roundings (bf16 out feeding D, bf16 P / dS as matrix operands,
     # bf16 storage) can sit more than one rounding step from the exact value
     # (tests/test_tolerance_model.py). Below |ref| = 2 the bar is the stated 2e-2.
+    # Where an element sums many terms (long rows, large GQA groups) the
+    # same roundings spread wider: the bar then also allows six standard
+    # deviations of their error (tests/test_tolerance_model.py pins the model).
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 7)
     tol = np.maximum(OUT_ATOL, 2.0 * ulp)
+    if sd is not None:
+        tol = np.maximum(tol, ulp / 2 + 6.0 * sd)
     worst = float((err / tol).max()) if err.size else 0.0
     nref = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))

@@ -31,18 +31,19 @@ def _check_bwd(bt, cp, ranks, tail=0):
         out, lse = H.run_fwd(meta, loc, bt, scale)
         dq, dks, dvs = H.run_bwd(meta, loc, bt, scale, out, lse)
         ref = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, want_grad=True)
+        sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
         tl = loc["t_local"]
-        H.compare_bf16("out", H.bf16_to_np(out)[:tl], ref["out"])
+        H.compare_bf16("out", H.bf16_to_np(out)[:tl], ref["out"], sd=sd["out"])
         dqb = H.bf16_to_np(dq)
-        st = H.compare_bf16("dq", dqb[:tl], ref["dq"])
+        st = H.compare_bf16("dq", dqb[:tl], ref["dq"], sd=sd["dq"])
         rows_r = O.shard_rows(bt.cu, bt.cup, cp, r)
         pad_r = ~O.valid_mask(bt.cu, bt.cup)[rows_r]
         assert not dqb[:tl][pad_r].any(), "dq padding rows must be exactly 0"
         for s in range(cp):
             dkb = H.bf16_to_np(dks[s])
             dvb = H.bf16_to_np(dvs[s])
-            a = H.compare_bf16(f"dk[{s}]", dkb[:tl], ref["dk_parts"][s])
-            b = H.compare_bf16(f"dv[{s}]", dvb[:tl], ref["dv_parts"][s])
+            a = H.compare_bf16(f"dk[{s}]", dkb[:tl], ref["dk_parts"][s], sd=sd["dk_parts"][s])
+            b = H.compare_bf16(f"dv[{s}]", dvb[:tl], ref["dv_parts"][s], sd=sd["dv_parts"][s])
             zero_rows = np.all(ref["dk_parts"][s] == 0, axis=(1, 2)) & np.all(ref["dv_parts"][s] == 0, axis=(1, 2))
             assert not dkb[:tl][zero_rows].any() and not dvb[:tl][zero_rows].any(), \
                 f"part {s}: rows no query of this rank reaches must be exactly 0"

@@ -30,9 +30,10 @@ def _check_fwd(bt, cp, ranks, tail=0, cup="copy"):
         meta, loc = H.local_inputs(db, cp, r, tail=tail, cup=cup)
         out, lse = H.run_fwd(meta, loc, bt, scale)
         ref = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, want_grad=False)
+        sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
         tl = loc["t_local"]
         ob = H.bf16_to_np(out)
-        st = H.compare_bf16("out", ob[:tl], ref["out"])
+        st = H.compare_bf16("out", ob[:tl], ref["out"], sd=sd["out"])
         lt = lse.cpu().numpy()
         sl = H.compare_lse("lse", lt[:, :tl], ref["lse"])
         rows = O.shard_rows(bt.cu, bt.cup, cp, r)
