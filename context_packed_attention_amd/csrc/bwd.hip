@@ -500,48 +500,6 @@ __global__ void __launch_bounds__(256) tail_zero_kernel(TailPtrs ptrs, int n_ptr
   }
 }
 
-// The dK/dV launches of all ring steps are independent of the dQ launches
-// (different outputs; both read what bwd_pre wrote), so they may run on a
-// second stream of the calling thread, forked from and joined back into the
-// caller's stream with events (a pattern graph capture records as a fork and
-// a join). One set per device and thread, default priority, kept for the
-// thread's lifetime.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-
-static cp_attn_status side_stream(int device, SideStream** out) {
-  static thread_local SideStream per_dev[64];
-  if (device < 0 || device >= 64) return fail(CP_ATTN_ERR_INVALID_ARG, "device index out of range");
-  SideStream& ss = per_dev[device];
-  if (!ss.s) {
-    cp_attn_status rc = hip_check(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking), "hipStreamCreate(side)");
-    if (rc == CP_ATTN_OK) rc = hip_check(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming), "hipEventCreate");
-    if (rc == CP_ATTN_OK) rc = hip_check(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming), "hipEventCreate");
-    if (rc != CP_ATTN_OK) {
-      if (ss.fork) (void)hipEventDestroy(ss.fork);
-      if (ss.s) (void)hipStreamDestroy(ss.s);
-      ss = SideStream{};
-      return rc;
-    }
-  }
-  *out = &ss;
-  return CP_ATTN_OK;
-}
-
-// compute units of a device (cached per device)
-static int cu_count(int device) {
-  static int cached[64] = {};
-  if (device < 0 || device >= 64) return 256;
-  if (!cached[device]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) n = 256;
-    cached[device] = n;
-  }
-  return cached[device];
-}
-
 static unsigned grid_for(long long n, int per_block) {
   long long b = (n + per_block - 1) / per_block;
   if (b < 1) b = 1;
@@ -614,20 +572,20 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     base.c_log2 = softmax_scale * LOG2E_F;
     base.dq_acc = dq_acc;
     const bool big = (long long)tl * hq * d * 2 >= (1ll << 31);  // local query tensors of 2 GiB or more
-    // Short launches (every dQ launch under four full waves of blocks) leave
-    // tails a concurrent chain can fill: then dK/dV runs on the side stream,
+    // The dK/dV launches of all ring steps are independent of the dQ launches
+    // (different outputs; both read what bwd_pre wrote). Short launches leave
+    // tails a concurrent chain can fill: then dK/dV runs on a side stream
     // forked from the caller's; long launches stay on one stream (co-resident
     // dK/dV and dQ blocks measured slower there).
     long long max_dq_blocks = 0;
     for (int i = 0; i < cp; ++i) max_dq_blocks = std::max<long long>(max_dq_blocks, m->sum.tiles_fwd[i] * hq);
-    const bool fork = max_dq_blocks < 4LL * 2 * cu_count(m->device);
-    SideStream* side = nullptr;
+    const bool fork = short_launches(max_dq_blocks, m->device);
+    SideSet* side = nullptr;
     hipStream_t sk = st;
     if (fork) {
-      if ((rc = side_stream(m->device, &side)) != CP_ATTN_OK) return rc;
-      sk = side->s;
-      if ((rc = hip_check(hipEventRecord(side->fork, st), "hipEventRecord(fork)")) != CP_ATTN_OK) return rc;
-      if ((rc = hip_check(hipStreamWaitEvent(sk, side->fork, 0), "hipStreamWaitEvent(fork)")) != CP_ATTN_OK) return rc;
+      if ((rc = side_set(m->device, &side)) != CP_ATTN_OK) return rc;
+      sk = side->s[0];
+      if ((rc = fork_to(side, st, 1)) != CP_ATTN_OK) return rc;
     }
     cp_attn_status lrc = CP_ATTN_OK;  // launch errors wait for the join
     for (int i = 0; i < cp && lrc == CP_ATTN_OK; ++i) {
@@ -674,10 +632,7 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
         if ((lrc = hip_check(hipGetLastError(), "bwd_dq launch")) != CP_ATTN_OK) break;
       }
     }
-    if (fork) {  // join
-      if ((rc = hip_check(hipEventRecord(side->join, sk), "hipEventRecord(join)")) != CP_ATTN_OK) return rc;
-      if ((rc = hip_check(hipStreamWaitEvent(st, side->join, 0), "hipStreamWaitEvent(join)")) != CP_ATTN_OK) return rc;
-    }
+    if (fork && (rc = join_from(side, st, 1)) != CP_ATTN_OK) return rc;
     if (lrc != CP_ATTN_OK) return lrc;
     timing_begin(st, "dq_finalize");
     hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for((long long)tl * hq * d / 4, 256)), dim3(256), 0, st, dq_acc,

@@ -263,6 +263,64 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(float* __restrict__ acc_
   }
 }
 
+// All step partials folded at once (the launches ran concurrently, each into
+// its own buffer): for every (row, head), the log-sum-exp of the steps that
+// cover the row and the correspondingly weighted outputs; writes the bf16
+// output and the final LSE for every local row (padding rows 0 / -inf).
+struct StepParts {
+  const float* o[CP_ATTN_MAX_CP];
+  const float* l[CP_ATTN_MAX_CP];
+  int kind[CP_ATTN_MAX_CP];
+};
+
+__global__ void __launch_bounds__(256) lse_merge_all_kernel(StepParts sp, int nsteps, const int32_t* __restrict__ rowflags,
+                                                            uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                                                            int t_local, int hq, int d, long long ld_lse_out) {
+  const long long q4_per_row = (long long)hq * d / 4;
+  const long long n = (long long)t_local * q4_per_row;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(e / q4_per_row);
+    const int off = (int)(e - (long long)t * q4_per_row) * 4;
+    const int h = off / d;
+    const int f = rowflags[t];
+    const bool valid = f & RF_VALID;
+    const long long li = (long long)h * t_local + t;
+    float m = NEG_INF_F;
+    if (valid)
+      for (int i = 0; i < nsteps; ++i)
+        if (sp.kind[i] != 2 || (f & RF_SECOND)) m = fmaxf(m, sp.l[i][li]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = NEG_INF_F;
+    if (m != NEG_INF_F) {
+      float ssum = 0.f;
+      for (int i = 0; i < nsteps; ++i) {
+        if (sp.kind[i] == 2 && !(f & RF_SECOND)) continue;
+        const float wgt = __expf(sp.l[i][li] - m);
+        const float4 o = *reinterpret_cast<const float4*>(sp.o[i] + (long long)t * hq * d + off);
+        ssum += wgt;
+        acc = make_float4(acc.x + wgt * o.x, acc.y + wgt * o.y, acc.z + wgt * o.z, acc.w + wgt * o.w);
+      }
+      const float inv = 1.f / ssum;
+      acc = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      lse = m + __logf(ssum);
+    }
+    uint2 pk;
+    pk.x = pack2_bf16(acc.x, acc.y);
+    pk.y = pack2_bf16(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(out + (long long)t * hq * d + off) = pk;
+    if ((off % d) == 0) lse_out[(long long)h * ld_lse_out + t] = lse;
+  }
+}
+
+// Whether the forward runs its ring steps concurrently (each into its own
+// partial buffer, merged once at the end): only for short launches.
+static bool fwd_forks(const cp_attn_meta* m, int hq) {
+  if (m->cp < 2) return false;
+  long long mx = 0;
+  for (int i = 0; i < m->cp; ++i) mx = std::max<long long>(mx, m->sum.tiles_fwd[i] * hq);
+  return short_launches(mx, m->device);
+}
+
 static cp_attn_status launch_fwd_step(const cp_attn_meta* m, int i, const FwdParams& base, int d, int tiles,
                                       hipStream_t st) {
   FwdParams p = base;
@@ -302,7 +360,8 @@ extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int
   const size_t o = tl * hq * d * sizeof(float);
   const size_t l = ((tl * hq * sizeof(float)) + 255) & ~size_t(255);
   const size_t o_al = (o + 255) & ~size_t(255);
-  if (pass == 0) return 2 * o_al + 2 * l;  // accumulator + step partial (out, lse)
+  if (pass == 0)  // accumulator + step partial (out, lse), or one partial per step when the steps run concurrently
+    return (fwd_forks(m, hq) ? (size_t)m->cp : 2) * (o_al + l);
   return o_al + 2 * l;                     // dq accumulator + per-row lse and -D = -rowsum(dO * O)
 }
 
@@ -362,6 +421,35 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   base.ld_o = (long long)hq * d;
   base.ld_lse = tl;
   const long long n4 = (long long)tl * hq * d / 4;
+  if (fwd_forks(m, hq)) {
+    // step i into partial i, the steps spread over the caller's stream and
+    // side streams forked from it, then one merge of all partials
+    SideSet* side = nullptr;
+    const int nside = std::min(m->cp - 1, MAX_SIDE);
+    if ((rc = side_set(m->device, &side)) != CP_ATTN_OK) return rc;
+    if ((rc = fork_to(side, st, nside)) != CP_ATTN_OK) return rc;
+    StepParts sp{};
+    cp_attn_status lrc = CP_ATTN_OK;  // launch errors wait for the join
+    for (int i = 0; i < m->cp && lrc == CP_ATTN_OK; ++i) {
+      const int s = m->sum.step_src[i];
+      FwdParams p = base;
+      p.k = (const uint16_t*)k_shards[s];
+      p.v = (const uint16_t*)v_shards[s];
+      p.o = (float*)(ws + (size_t)i * o_al);
+      p.lse = (float*)(ws + (size_t)m->cp * o_al + (size_t)i * l_al);
+      sp.o[i] = p.o;
+      sp.l[i] = p.lse;
+      sp.kind[i] = m->sum.step_kind[i];
+      lrc = launch_fwd_step(m, i, p, d, (int)m->sum.tiles_fwd[i], i == 0 ? st : side->s[(i - 1) % nside]);
+    }
+    if ((rc = join_from(side, st, nside)) != CP_ATTN_OK) return rc;
+    if (lrc != CP_ATTN_OK) return lrc;
+    timing_begin(st, "lse_merge_all");
+    hipLaunchKernelGGL(lse_merge_all_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, sp, m->cp, rowflags,
+                       (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
+    timing_end(st);
+    return hip_check(hipGetLastError(), "lse_merge launch");
+  }
   for (int i = 0; i < m->cp; ++i) {
     const int s = m->sum.step_src[i];
     FwdParams p = base;

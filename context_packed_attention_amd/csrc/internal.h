@@ -89,6 +89,22 @@ struct cp_attn_meta {
 
 namespace cpattn {
 
+// side streams of the calling thread (streams.hip)
+constexpr int MAX_SIDE = 4;
+struct SideSet {
+  bool ready = false;
+  hipStream_t s[MAX_SIDE] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[MAX_SIDE] = {};
+};
+cp_attn_status side_set(int device, SideSet** out);
+cp_attn_status fork_to(SideSet* ss, hipStream_t st, int n);
+cp_attn_status join_from(SideSet* ss, hipStream_t st, int n);
+int cu_count(int device);
+// launches this short (under four full waves of two blocks per compute
+// unit) leave tails that concurrent independent launches can fill
+bool short_launches(long long max_blocks, int device);
+
 // per-kernel event timing (no-ops unless enabled through the C ABI)
 void timing_begin(hipStream_t st, const char* name);
 void timing_end(hipStream_t st);

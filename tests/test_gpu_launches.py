@@ -2,7 +2,8 @@
 every launch per kernel):
 
 * ring completeness: one forward kernel, one dK/dV and one dQ kernel per ring
-  step, CP-1 merges (a CP path that silently drops ring steps runs fast with
+  step, and either CP-1 pairwise merges or (steps run concurrently) one merge
+  of all step partials (a CP path that silently drops ring steps runs fast with
   wrong gradients - "Hybrid / Hierarchical Context Parallel Skill", Pitfalls);
 * the padding decision by value gives the same launch sequence for an
   aliased, NULL or distinct-equal cu_seqlens_padded;
@@ -43,7 +44,10 @@ def test_ring_completeness(cfg):
         n = _launches(bt, cp, r)
         H.log(f"[launch] cfg{cfg} rank {r}: {n}")
         assert n["fwd_step"] == cp and n["bwd_dkdv"] == cp and n["bwd_dq"] == cp
-        assert n["lse_merge"] == max(1, cp - 1)
+        if "lse_merge_all" in n:
+            assert n["lse_merge_all"] == 1 and "lse_merge" not in n and cp > 1
+        else:
+            assert n["lse_merge"] == max(1, cp - 1)
         assert n["bwd_pre"] == 1 and n["dq_finalize"] == 1
         assert "tail_zero" not in n
 
