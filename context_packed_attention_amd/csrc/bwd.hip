@@ -92,7 +92,7 @@ template <int D>
 __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdParams p) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
-  using KCopy = TileCopy<D, false, BN, NWAVES>;
+  using KCopy = TileCopy<D, false, BN, NWAVES, true>;  // K read both ways: permuted rows (V too, same plan)
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][KCopy::BYTES / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][KCopy::BYTES / 2];
 
@@ -161,8 +161,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
-          dp[mb] = mfma32x32x16(lds_read_row<D>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
+          s[mb] = mfma32x32x16(lds_read_row<D, true>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
+          dp[mb] = mfma32x32x16(lds_read_row<D, true>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
         }
       }
       if (p.causal && k0 + BN - 1 > wrow_lo) {
@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
         const bf16x8_t ds = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
         for (int md = 0; md < NMD; ++md)
-          acc[md] = mfma32x32x16(lds_read_tr<D, false>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
+          acc[md] = mfma32x32x16(lds_read_tr<D, false, true>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
       }
     }
   }
@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
   constexpr int KB = DKDV_KB;
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
-  using QCopy = TileCopy<D, false, BQ, NWAVES>;
+  using QCopy = TileCopy<D, false, BQ, NWAVES, true>;  // Q and dO read both ways: permuted rows
   using VCopy = TileCopy<D, false, BK, NWAVES>;
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][QCopy::BYTES / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][QCopy::BYTES / 2];
@@ -369,8 +369,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
         }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8_t qa = lds_read_row<D>(Qs[buf], l32, 2 * kk + g);
-          const bf16x8_t da = lds_read_row<D>(Ds[buf], l32, 2 * kk + g);
+          const bf16x8_t qa = lds_read_row<D, true>(Qs[buf], l32, 2 * kk + g);
+          const bf16x8_t da = lds_read_row<D, true>(Ds[buf], l32, 2 * kk + g);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             s[kb] = mfma32x32x16(qa, kf[kb][kk], s[kb]);
@@ -415,8 +415,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
           }
 #pragma unroll
           for (int md = 0; md < NMD; ++md) {
-            const bf16x8_t ta = lds_read_tr<D, false>(Ds[buf], kq * 16, md * 32, lane);
-            const bf16x8_t tq = lds_read_tr<D, false>(Qs[buf], kq * 16, md * 32, lane);
+            const bf16x8_t ta = lds_read_tr<D, false, true>(Ds[buf], kq * 16, md * 32, lane);
+            const bf16x8_t tq = lds_read_tr<D, false, true>(Qs[buf], kq * 16, md * 32, lane);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
               dv[kb][md] = mfma32x32x16(ta, pb[kb], dv[kb][md]);

@@ -122,15 +122,25 @@ __device__ __forceinline__ void map_block(int bid, int nheads, int& item, int& h
 // transposing ds_read_b64_tr_b16 serves 32 lanes per cycle. Row strides:
 //  * tiles read by b128 row reads (16 lanes = one 16-byte unit of 16
 //    consecutive rows), alone or together with transposing reads: 304 bytes
-//    (D = 128) or 144 (D = 64) - conflict-free for the row reads, while a
-//    transposing read pays about 1.6 extra cycles;
+//    (D = 128) or 144 (D = 64) - conflict-free for the row reads;
 //  * tiles read only by transposing reads (32 lanes take 64 consecutive bytes
-//    of 4 consecutive rows, first row a multiple of 4): 320 bytes (D = 128)
-//    or 192 (D = 64) - conflict-free.
-// Padding (no XOR swizzle) keeps every address linear in the unrolled loop
-// indices, so the compiler folds them into instruction offsets; a swizzle
-// that removed both kinds of conflict measured slower for its extra address
-// arithmetic.
+//    of 4 rows): 320 bytes (D = 128) or 192 (D = 64) - conflict-free for 4
+//    consecutive rows.
+// A transposing read of 4 consecutive rows 304 (144) bytes apart hits each
+// bank twice (measured: 4.1 instead of 2.3 cycles per instruction per CU).
+// Tiles read both ways therefore store their rows permuted inside each
+// 16-row block (perm_row below): the 4 logical rows a transposing read takes
+// then sit 4 physical rows apart, 4 x 304 (144) bytes = 16 x odd banks, which
+// is conflict-free, and the 16 rows a row read takes are still 16 distinct
+// rows of one block. Padding and the permutation keep every address linear in
+// the unrolled loop indices (only the per-lane base changes), so the compiler
+// folds them into instruction offsets; an XOR swizzle that removed both kinds
+// of conflict measured slower for its extra address arithmetic.
+// Physical row of logical row r in a permuted tile: within each 16-row block
+// (r = 16 b + 4 a + c) row 16 b + 4 c + a, a 4 x 4 transpose and its own
+// inverse.
+__host__ __device__ constexpr int perm_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
 template <int D, bool TR_ONLY>
 __host__ __device__ constexpr int tile_rowb() { return TR_ONLY ? (D == 128 ? 320 : 192) : (D == 128 ? 304 : 144); }
 
@@ -159,8 +169,9 @@ constexpr int OOB_OFFSET = 0x7ffffff0;  // any offset past num_records reads zer
 // offset past any buffer's end and load zeros). Each copy takes a buffer
 // resource whose base is the tile's first row and whose size ends at the
 // range's end, so rows past the range load zeros.
-template <int D, bool TR_ONLY, int ROWS, int NW>
+template <int D, bool TR_ONLY, int ROWS, int NW, bool PERM = false>
 struct TileCopy {
+  static_assert(!PERM || ROWS % 16 == 0, "permuted tiles hold whole 16-row blocks");
   static constexpr int SU = tile_rowb<D, TR_ONLY>() / 16;  // units per padded row
   static constexpr int UPR = D * 2 / 16;                   // units per data row
   static constexpr int UNITS = ROWS * SU;
@@ -174,7 +185,8 @@ struct TileCopy {
     for (int cc = 0; cc < PER_WAVE; ++cc) {
       const int u = (cc * NW + wave) * 64 + lane;
       const int row = u / SU, unit = u % SU;
-      voff[cc] = (unit < UPR && u < UNITS) ? row * ld_bytes + unit * 16 : OOB_OFFSET;
+      const int src = PERM ? perm_row(row) : row;  // perm_row is an involution
+      voff[cc] = (unit < UPR && u < UNITS) ? src * ld_bytes + unit * 16 : OOB_OFFSET;
     }
   }
   __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rsrc, void* lds_tile, int wave) const {
@@ -203,10 +215,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const void* base, lo
   return make_rsrc(reinterpret_cast<const char*>(base) + off_bytes, n <= 0 ? 0 : (n < RSRC_CAP ? n : RSRC_CAP));
 }
 
-// b128 read of 16-byte unit `unit` of `row` (tiles with row reads).
-template <int D>
+// b128 read of 16-byte unit `unit` of logical row `row` (tiles with row
+// reads; PERM for tiles stored with permuted rows).
+template <int D, bool PERM = false>
 __device__ __forceinline__ bf16x8_t lds_read_row(const uint16_t* tile, int row, int unit) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + row * tile_rowb<D, false>() +
+  const int prow = PERM ? perm_row(row) : row;
+  return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + prow * tile_rowb<D, false>() +
                                                    unit * 16));
 }
 
@@ -216,15 +230,19 @@ __device__ __forceinline__ bf16x8_t lds_read_row(const uint16_t* tile, int row, 
 // a multiple of 16). Within each 16-lane group, lane j supplies the address
 // of row (first + j / 4), columns 4 (j % 4) .. +3 of its 16-column half; the
 // hardware hands lane j column j of those four rows.
-template <int D, bool TR_ONLY>
+// In a permuted tile (PERM) logical rows k0 + 4 g + (i / 4) and k0 + 8 + 4 g +
+// (i / 4) sit at physical rows k0 + 4 (i / 4) + g and 2 rows further on.
+template <int D, bool TR_ONLY, bool PERM = false>
 __device__ __forceinline__ bf16x8_t lds_read_tr(const uint16_t* tile, int k0, int col0, int lane) {
+  static_assert(!(PERM && TR_ONLY), "permuted tiles use the row-read stride");
   constexpr int ROWB = tile_rowb<D, TR_ONLY>();
   const int i = lane & 15, h = (lane >> 4) & 1, g = lane >> 5;
   const int col = col0 + 16 * h + 4 * (i & 3);
-  const int r0 = k0 + 4 * g + (i >> 2);
+  const int r0 = PERM ? k0 + 4 * (i >> 2) + g : k0 + 4 * g + (i >> 2);
   const char* base = reinterpret_cast<const char*>(tile) + r0 * ROWB + col * 2;
   i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(base));
-  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(base + 8 * ROWB));
+  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(base + (PERM ? 2 : 8) * ROWB));
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
