@@ -377,6 +377,16 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
             dp[kb] = mfma32x32x16(da, lds_read_row<D>(Vt, wr0 + kb * 32 + l32, 2 * kk + g), dp[kb]);
           }
         }
+        // the first query slice's transposed fragments are read now, so
+        // their LDS latency hides behind the softmax (the scheduling fence
+        // keeps the compiler from sinking the reads again)
+        bf16x8_t ta0[NMD], tq0[NMD];
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) {
+          ta0[md] = lds_read_tr<D, false, true>(Ds[buf], 0, md * 32, lane);
+          tq0[md] = lds_read_tr<D, false, true>(Qs[buf], 0, md * 32, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (p.causal && qlo < wkey_hi) {
           // query rows before a lane's key (a real branch, kept out of
           // if-conversion; only a wavefront's first tiles take it)
@@ -415,8 +425,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
           }
 #pragma unroll
           for (int md = 0; md < NMD; ++md) {
-            const bf16x8_t ta = lds_read_tr<D, false, true>(Ds[buf], kq * 16, md * 32, lane);
-            const bf16x8_t tq = lds_read_tr<D, false, true>(Qs[buf], kq * 16, md * 32, lane);
+            const bf16x8_t ta = kq == 0 ? ta0[md] : lds_read_tr<D, false, true>(Ds[buf], kq * 16, md * 32, lane);
+            const bf16x8_t tq = kq == 0 ? tq0[md] : lds_read_tr<D, false, true>(Qs[buf], kq * 16, md * 32, lane);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
               dv[kb][md] = mfma32x32x16(ta, pb[kb], dv[kb][md]);

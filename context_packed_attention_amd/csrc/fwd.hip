@@ -117,6 +117,15 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       for (int mb = 0; mb < 2; ++mb)
         s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
     }
+    // all V fragments of the tile are read now, so the LDS latency hides
+    // behind the softmax instead of stalling the P V products (the
+    // scheduling fence keeps the compiler from sinking the reads again)
+    bf16x8_t vf[4][NMD];
+#pragma unroll
+    for (int kk2 = 0; kk2 < 4; ++kk2)
+#pragma unroll
+      for (int md = 0; md < NMD; ++md) vf[kk2][md] = lds_read_tr<D, true>(Vs[buf], kk2 * 16, md * 32, lane);
+    __builtin_amdgcn_sched_barrier(0);
     if (masked) {
       // a real branch (kept out of if-conversion), taken on few tiles
       __asm__ volatile("" ::: "memory");
@@ -161,7 +170,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
       for (int md = 0; md < NMD; ++md)
-        o[md] = mfma32x32x16(lds_read_tr<D, true>(Vs[buf], kk2 * 16, md * 32, lane), pb, o[md]);
+        o[md] = mfma32x32x16(vf[kk2][md], pb, o[md]);
     }
   };
 
