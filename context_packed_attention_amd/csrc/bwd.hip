@@ -147,9 +147,12 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
     const int buf = kt & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
     const int k0 = kt * BN;
     const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
+    // the next tile's copy is issued after this tile's score products (the
+    // address arithmetic then fills the wait for their results); idle
+    // wavefronts issue their share at once
+    if (!active && kt + 1 < nt) issue(kt + 1, buf ^ 1);
     if (active) {
       f32x16_t s[2], dp[2];
 #pragma unroll
@@ -165,6 +168,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
           dp[mb] = mfma32x32x16(lds_read_row<D, true>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
         }
       }
+      if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
       if (p.causal && k0 + BN - 1 > wrow_lo) {
         // keys after the lane's row (a real branch, kept out of
         // if-conversion; only the tiles on a wavefront's diagonal take it)
