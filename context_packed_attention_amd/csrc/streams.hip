@@ -1,11 +1,15 @@
 // Side streams for running independent launches of one call concurrently:
 // per calling thread and device, a few streams of default priority with a
-// fork event and one join event each, created on first use and kept for the
-// thread's lifetime. A fork is an event recorded on the caller's stream that
+// fork event and one join event each, created on first use and never
+// released (a thread-exit hook could run after the HIP runtime has shut down
+// at process exit; each thread that calls the library on a device holds
+// four streams and five events there until the process ends). A fork is an event recorded on the caller's stream that
 // the side streams wait on; a join records an event on every side stream
 // that the caller's stream waits on (graph capture records the same pattern
 // as a fork and a join).
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 
 #include "internal.h"
 
@@ -58,14 +62,14 @@ cp_attn_status join_from(SideSet* ss, hipStream_t st, int n) {
 }
 
 int cu_count(int device) {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   if (device < 0 || device >= 64) return 256;
-  if (!cached[device]) {
-    int n = 0;
+  int n = cached[device].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) n = 256;
-    cached[device] = n;
+    cached[device].store(n, std::memory_order_relaxed);
   }
-  return cached[device];
+  return n;
 }
 
 bool short_launches(long long max_blocks, int device) { return max_blocks < 4LL * 2 * cu_count(device); }
