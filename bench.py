@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--a2a", action="store_true",
                     help="only time the hierarchical front end's all-to-all (sequence split -> head split and back) "
                          "on the 64K hierarchical pack, [a2a, p2p] = [2, 2], Q of 32 heads, and exit")
+    ap.add_argument("--all-gather", action="store_true",
+                    help="time the all-gather share of the selected workload instead (gathered K/V in, the rank's "
+                         "contribution to every gathered dK/dV row out) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and exit "
                          "(the known-size reference for the HBM byte counters)")
@@ -196,6 +199,85 @@ def a2a_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def ag_bench(args):
+    """All-gather share of the selected workload: the rank's queries against
+    the gathered K/V (metadata build + forward + backward per step), the same
+    attention pairs as the ring share plus the shard-view gather and the
+    dK/dV scatter."""
+    import numpy as np
+    import torch
+    from context_packed_attention_amd import api, synth
+    w = synth.workload(args.workload)
+    rank = w["ranks"][-1] if args.workload != 1 else 0
+    batch, _ = synth.make_workload(args.workload)
+    cp, hq, hkv, d = w["cp"], w["hq"], w["hkv"], w["d"]
+    scale = 1.0 / math.sqrt(d)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    cu = torch.tensor(batch.cu, dtype=torch.int32, device="cuda")
+    cup = torch.tensor(batch.cup, dtype=torch.int32, device="cuda")
+    T = batch.total_rows
+    t_alloc = T // cp
+    meta = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc)
+    gq, gdo = dev_bf16(batch.q), dev_bf16(batch.do)
+    k_full, v_full = dev_bf16(batch.k), dev_bf16(batch.v)
+    q = torch.empty((t_alloc, hq, d), dtype=torch.bfloat16, device="cuda")
+    do = torch.empty_like(q)
+    api.cp_attn_shard_gather(meta, rank, gq, q, hq * d * 2)
+    api.cp_attn_shard_gather(meta, rank, gdo, do, hq * d * 2)
+    del gq, gdo
+    out = torch.empty_like(q)
+    lse = torch.empty((hq, t_alloc), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dk_full = torch.empty_like(k_full)
+    dv_full = torch.empty_like(v_full)
+    ws_f = torch.empty(api.cp_attn_ag_workspace_bytes(meta, hq, hkv, d, 0), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(api.cp_attn_ag_workspace_bytes(meta, hq, hkv, d, 1), dtype=torch.uint8, device="cuda")
+    pairs = sum(api.step_pairs(meta))
+    meta.close()
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        m = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+        api.cp_attn_ag_fwd(m, q, k_full, v_full, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream)
+        api.cp_attn_ag_bwd(m, q, k_full, v_full, out, lse, do, hq, hkv, d, scale, 1, dq, dk_full, dv_full, ws_b,
+                           stream=stream)
+        return m
+
+    held = [one_step() for _ in range(args.warmup)]
+    torch.cuda.synchronize()
+    for m in held:
+        m.close()
+    held = []
+    api.cp_attn_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        held.append(one_step())
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    api.cp_attn_timing_enable(False)
+    per_kernel = api.cp_attn_timing_read()
+    for m in held:
+        m.close()
+    ms = (t1 - t0) * 1e3 / args.steps
+    tflops = 14 * d * hq * pairs / (ms * 1e-3) / 1e12
+    kernels = {k: {"launches_per_step": v[1] / args.steps, "ms_per_step": v[0] / args.steps}
+               for k, v in per_kernel.items()}
+    line = {
+        "metric": "all-gather CP share: attention fwd+bwd TFLOP/s (1 MI355X)",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO)",
+        "config": {"workload": w["name"] + "-allgather", "cp_size": cp, "cp_rank": rank, "hq": hq, "hkv": hkv,
+                   "head_dim": d, "gathered_rows": T, "pairs": pairs},
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -217,6 +299,9 @@ def main():
         return
     if args.a2a:
         a2a_bench(args)
+        return
+    if args.all_gather:
+        ag_bench(args)
         return
     w = synth.workload(args.workload)
     rank = w["ranks"][-1] if args.workload != 1 else 0

@@ -24,6 +24,7 @@ EXPORTED = [
     "cp_attn_timing_enable", "cp_attn_timing_read",
     "cp_attn_graph_capture", "cp_attn_graph_launch", "cp_attn_graph_kernels", "cp_attn_graph_free",
     "cp_attn_a2a_seq_to_head", "cp_attn_a2a_head_to_seq",
+    "cp_attn_ag_workspace_bytes", "cp_attn_ag_fwd", "cp_attn_ag_bwd",
 ]
 
 
@@ -86,6 +87,13 @@ def load(path: str | None = None) -> C.CDLL:
     for f in (lib.cp_attn_a2a_seq_to_head, lib.cp_attn_a2a_head_to_seq):
         f.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
         f.restype = st
+    lib.cp_attn_ag_workspace_bytes.argtypes = [vp, i32, i32, i32, i32]
+    lib.cp_attn_ag_workspace_bytes.restype = C.c_size_t
+    lib.cp_attn_ag_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, C.c_float, i32, vp, vp, vp, C.c_size_t, vp]
+    lib.cp_attn_ag_fwd.restype = st
+    lib.cp_attn_ag_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, C.c_float, i32, vp, vp, vp, vp,
+                                   C.c_size_t, vp]
+    lib.cp_attn_ag_bwd.restype = st
     lib.cp_attn_last_error.argtypes = []
     lib.cp_attn_last_error.restype = C.c_char_p
     _lib = lib

@@ -280,3 +280,28 @@ def cp_attn_a2a_head_to_seq(meta: Meta, a2a_size: int, p2p_rank: int, heads: int
     rc = L.load().cp_attn_a2a_head_to_seq(meta.handle, int(a2a_size), int(p2p_rank), int(heads), int(head_bytes),
                                           _ptr_array(ins), _ptr_array(outs), _stream(stream))
     _check(rc, "cp_attn_a2a_head_to_seq")
+
+
+def cp_attn_ag_workspace_bytes(meta: Meta, hq: int, hkv: int, d: int, pass_: int) -> int:
+    return int(L.load().cp_attn_ag_workspace_bytes(meta.handle, hq, hkv, d, pass_))
+
+
+def cp_attn_ag_fwd(meta: Meta, q, k_full, v_full, hq: int, hkv: int, d: int, softmax_scale: float, causal: int,
+                   out, lse, workspace, stream=None):
+    """All-gather share, forward: k_full / v_full are the gathered K / V in
+    packed (cu_seqlens_padded) order."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = L.load().cp_attn_ag_fwd(meta.handle, _ptr(q), _ptr(k_full), _ptr(v_full), hq, hkv, d, float(softmax_scale),
+                                 int(causal), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "cp_attn_ag_fwd")
+
+
+def cp_attn_ag_bwd(meta: Meta, q, k_full, v_full, out, lse, dout, hq: int, hkv: int, d: int, softmax_scale: float,
+                   causal: int, dq, dk_full, dv_full, workspace, stream=None):
+    """All-gather share, backward: dk_full / dv_full receive this rank's
+    contribution to every gathered key row."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = L.load().cp_attn_ag_bwd(meta.handle, _ptr(q), _ptr(k_full), _ptr(v_full), _ptr(out), _ptr(lse), _ptr(dout),
+                                 hq, hkv, d, float(softmax_scale), int(causal), _ptr(dq), _ptr(dk_full),
+                                 _ptr(dv_full), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "cp_attn_ag_bwd")

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
-SOURCES = ["meta.hip", "fwd.hip", "bwd.hip", "timing.hip", "graph.hip", "a2a.hip", "streams.hip"]
+SOURCES = ["meta.hip", "fwd.hip", "bwd.hip", "timing.hip", "graph.hip", "a2a.hip", "streams.hip", "ag.hip"]
 ARCH = "gfx950"
 
 

@@ -128,6 +128,11 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   f32x16_t acc[NMD];
 #pragma unroll
   for (int md = 0; md < NMD; ++md) acc[md] = zero16();
+  // -D of the lane's row: every dP^T chain starts from it (the first MFMA
+  // reads it as its accumulator input, so dP^T - D costs no VALU)
+  f32x16_t negd16;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) negd16[j] = -dq_d;
 
   const int ldb = (int)(p.ld_kv * 2);
   const long long kv_end = (long long)kl * ldb;
@@ -158,7 +163,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         s[mb] = zero16();
-        dp[mb] = zero16();
+        dp[mb] = negd16;
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -184,7 +189,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float pv = fast_exp2(fmaf(s[mb][j], c, -lse2));
-          s[mb][j] = pv * (dp[mb][j] - dq_d);  // dS^T
+          s[mb][j] = pv * dp[mb][j];  // dS^T = P (dP - D)
         }
 #pragma unroll
       for (int kk2 = 0; kk2 < BN / 16; ++kk2) {

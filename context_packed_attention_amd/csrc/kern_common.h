@@ -116,6 +116,29 @@ __device__ __forceinline__ void map_block(int bid, int nheads, int& item, int& h
   }
 }
 
+// Copy `units` 16-byte units from src to dst with the 64 lanes of a
+// wavefront, four loads in flight per lane before their stores; the data is
+// touched once, so both sides bypass cache retention (non-temporal).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void wave_copy(const uint4* __restrict__ src_, uint4* __restrict__ dst_, int units, int lane) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(src_);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(dst_);
+  for (int base = 0; base < units; base += 256) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = base + i * 64 + lane;
+      if (u < units) v[i] = __builtin_nontemporal_load(src + u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = base + i * 64 + lane;
+      if (u < units) __builtin_nontemporal_store(v[i], dst + u);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // Row-major tiles (rows x D bf16) live in LDS with padded rows. gfx950's LDS
 // has 64 banks of 4 bytes; a b128 read serves 16 lanes per cycle and the

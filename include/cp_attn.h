@@ -195,6 +195,43 @@ cp_attn_status cp_attn_shard_gather(const cp_attn_meta* m, int32_t shard, const 
                                     void* local, size_t row_bytes, void* stream);
 
 /*
+ * One rank's share under all-gather context parallelism ([I3] "Implementation
+ * Map": "all_gather" is one of the cp_comm_type values). Reading (the pages
+ * name the type and nothing more): every rank first holds the gathered K/V of
+ * the whole packed batch, computes its own query chunks against it, and its
+ * contribution to the gradient of every gathered key row is what a
+ * reduce-scatter across ranks would then sum. The attended pairs are the ring
+ * share's, so these calls gather the shard views out of the gathered K/V (an
+ * HBM-bound permutation into the workspace), run the ring-step kernels of
+ * cp_attn_fwd / cp_attn_bwd, and the backward scatters the per-shard dK/dV
+ * parts back to gathered rows (a permutation: each gathered row belongs to one
+ * shard).
+ *
+ *  m                  metadata of this rank (cp_attn_rank_metadata)
+ *  q, out, lse, dout, dq   this rank's local tensors, as for cp_attn_fwd/bwd
+ *  k_full, v_full     gathered K / V, bf16 [cu_seqlens_padded[B], hkv, d] in
+ *                     packed (cu_seqlens_padded) order, 16-byte aligned
+ *  dk_full, dv_full   bf16 [cu_seqlens_padded[B], hkv, d] (overwritten: every
+ *                     row [0, cu_seqlens_padded[B]) is written; rows of keys
+ *                     no query of this rank reaches, and padding rows, are 0;
+ *                     rows past cu_seqlens_padded[B] are not touched)
+ *  workspace          device scratch of cp_attn_ag_workspace_bytes(m, hq, hkv,
+ *                     d, pass) bytes (pass 0 forward, 1 backward), 256-byte
+ *                     aligned: the shard views (and gradient parts) of t_alloc
+ *                     rows each, then the ring steps' own workspace
+ * Other arguments and errors as cp_attn_fwd / cp_attn_bwd. Never
+ * synchronises; capturable in a HIP graph.
+ */
+size_t cp_attn_ag_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, int32_t d, int32_t pass);
+cp_attn_status cp_attn_ag_fwd(const cp_attn_meta* m, const void* q, const void* k_full, const void* v_full,
+                              int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal, void* out,
+                              float* lse, void* workspace, size_t ws_bytes, void* stream);
+cp_attn_status cp_attn_ag_bwd(const cp_attn_meta* m, const void* q, const void* k_full, const void* v_full,
+                              const void* out, const float* lse, const void* dout, int32_t hq, int32_t hkv, int32_t d,
+                              float softmax_scale, int32_t causal, void* dq, void* dk_full, void* dv_full,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * The all-to-all of one a2a group of hierarchical (a2a + p2p) context
  * parallelism, played on one device. [I3] "Enablement" and "Implementation
  * Map": CP = a2a size x p2p size and every padded length divides by 2*CP;

@@ -21,6 +21,10 @@ What is computed is the plain definition, written out slowly in float64 numpy:
   row / head permutation: page "Hybrid / Hierarchical Context Parallel Skill",
   sections "Enablement" and "Implementation Map" (CP = a2a size x p2p size);
   the rank numbering inside the group is a reading, stated where it is coded.
+* The all-gather variant's layout of a rank's dK/dV contribution (every key row
+  of the packed batch in global order): the same page, section "Implementation
+  Map", names "all_gather" among the communication types; the layout is a
+  reading (the rank holds the gathered K/V).
 
 Readings taken where the pages are silent (each is listed in the design notes):
 padding sits at the end of each sequence's padded slot; valid rows fill the
@@ -31,7 +35,8 @@ rank's query rows only.
 
 Parity is pinned by the "not gpu" tests: brute force over an explicit mask of
 the whole pack, torch's fp64 CPU attention routine (out and LSE) and autograd,
-central finite differences, closed forms and the all-ranks invariants; the
+central finite differences, closed forms and the all-ranks invariants (the
+gathered-layout contributions of all ranks sum to the whole pack's gradient); the
 all-to-all by the identity "CP-level shards, then the group's all-to-all =
 the p2p-level shard, split by heads" and its inverse.
 """
@@ -386,7 +391,12 @@ def share(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: floa
     Returns a dict with out [T_local, Hq, D], lse [Hq, T_local], and if asked
     dq [T_local, Hq, D] and dk_parts / dv_parts: a list over source shards s of
     [T_local, Hkv, D] arrays, the contribution of r's query rows to the
-    gradient of shard s's keys and values, in shard s's local layout.
+    gradient of shard s's keys and values, in shard s's local layout; plus
+    dk_full / dv_full [T, Hkv, D]: the same contribution for every key row of
+    the packed batch in its global order (the all-gather variant's layout:
+    rank r holds the gathered K/V, page "Hybrid / Hierarchical Context
+    Parallel Skill", section "Implementation Map", names "all_gather" as a
+    communication type).
     Inputs are bf16 bit arrays in the global packed layout.
     """
     cu, cup = validate(cu, cup, cp, r)
@@ -403,6 +413,8 @@ def share(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: floa
         outd["dq"] = res[2][own]
         outd["dk_parts"] = [res[3][shard_rows(cu, cup, cp, s)] for s in range(cp)]
         outd["dv_parts"] = [res[4][shard_rows(cu, cup, cp, s)] for s in range(cp)]
+        outd["dk_full"] = res[3]
+        outd["dv_full"] = res[4]
     return outd
 
 
@@ -425,8 +437,9 @@ def share_rounding_sd(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int,
       and dK_j through -scale sum_i P_ij D_i Q_i (independent per row i).
 
     Returns {"out", "dq": [T_local, Hq, D], "dk_parts", "dv_parts": lists of
-    [T_local, Hkv, D]} in rank r's / shard s's local layouts (0 where an
-    element is not computed).
+    [T_local, Hkv, D]} in rank r's / shard s's local layouts, and "dk_full",
+    "dv_full" [T, Hkv, D] in the global order (0 where an element is not
+    computed).
     """
     cu, cup = validate(cu, cup, cp, r)
     q = bf16_to_f64(q_bits)
@@ -469,7 +482,8 @@ def share_rounding_sd(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int,
     own = shard_rows(cu, cup, cp, r)
     return {"out": np.sqrt(var_out[own]), "dq": np.sqrt(var_dq[own]),
             "dk_parts": [np.sqrt(var_dk[shard_rows(cu, cup, cp, s)]) for s in range(cp)],
-            "dv_parts": [np.sqrt(var_dv[shard_rows(cu, cup, cp, s)]) for s in range(cp)]}
+            "dv_parts": [np.sqrt(var_dv[shard_rows(cu, cup, cp, s)]) for s in range(cp)],
+            "dk_full": np.sqrt(var_dk), "dv_full": np.sqrt(var_dv)}
 
 
 class _HeadCache:
