@@ -106,7 +106,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
   // one key tile; masking runs only on a wavefront's last tiles (keys past
   // the range, or at the causal step keys after its first row)
-  auto key_tile = [&](int kt, int buf, bool masked) {
+  // first half of a key tile: scores, V fragments, softmax; P packed to bf16
+  auto key_tile = [&](int kt, int buf, bool masked, bf16x8_t (&pb)[4], bf16x8_t (&vf)[4][NMD]) {
     const int k0 = kt * BN;
     f32x16_t s[2];
     s[0] = zero16();
@@ -120,7 +121,6 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     // all V fragments of the tile are read now, so the LDS latency hides
     // behind the softmax instead of stalling the P V products (the
     // scheduling fence keeps the compiler from sinking the reads again)
-    bf16x8_t vf[4][NMD];
 #pragma unroll
     for (int kk2 = 0; kk2 < 4; ++kk2)
 #pragma unroll
@@ -166,25 +166,40 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       }
     l_run += lsum;
 #pragma unroll
-    for (int kk2 = 0; kk2 < 4; ++kk2) {
-      const bf16x8_t pb = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
+    for (int kk2 = 0; kk2 < 4; ++kk2) pb[kk2] = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
+  };
+  // second half: O += P V from registers
+  auto pv_tile = [&](const bf16x8_t (&pb)[4], const bf16x8_t (&vf)[4][NMD]) {
 #pragma unroll
-      for (int md = 0; md < NMD; ++md)
-        o[md] = mfma32x32x16(vf[kk2][md], pb, o[md]);
-    }
+    for (int kk2 = 0; kk2 < 4; ++kk2)
+#pragma unroll
+      for (int md = 0; md < NMD; ++md) o[md] = mfma32x32x16(vf[kk2][md], pb[kk2], o[md]);
   };
 
-  if (nt > 0) issue(0, 0);
+  // Tile kt's buffers are free once its scores and V fragments have been
+  // read, so the block synchronises there (not at the top of the next
+  // iteration): that barrier also publishes tile kt + 1's copy, and tile kt +
+  // 2's copy goes into the freed buffers right after it. The P V products of
+  // tile kt and the scores of tile kt + 1 then follow each other with no
+  // barrier between.
+  if (nt > 0) {
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nt > 1) issue(1, 1);
+  }
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
     const int k0 = kt * BN;
     const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
     const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
-    if (active) key_tile(kt, buf, need_mask);
+    bf16x8_t pb[4], vf[4][NMD];
+    if (active) key_tile(kt, buf, need_mask, pb, vf);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 2 < nt) issue(kt + 2, buf);
+    if (active) pv_tile(pb, vf);
   }
 
   const float lt = sum_halves(l_run);
