@@ -26,6 +26,7 @@ CASES = [
     ("ag-ragged-cp3-d128-gqa", [600, 1, 250, 0], [600, 12, 252, 6], 3, 8, 2, 128, 37),
     ("ag-tiny-cp4-d64-pad", [5, 9, 1], [8, 16, 8], 4, 2, 2, 64, 0),
     ("ag-long-cp4-d128", [1800, 500], [1808, 504], 4, 4, 4, 128, 0),
+    ("ag-cp1-d128", [300, 77], [304, 80], 1, 2, 1, 128, 5),
 ]
 
 
@@ -97,4 +98,50 @@ def test_ag_argument_errors():
     ws = torch.empty(api.cp_attn_ag_workspace_bytes(meta, 2, 2, 64, 0), dtype=torch.uint8, device="cuda")
     with pytest.raises(api.CpAttnError):
         api.cp_attn_ag_fwd(meta, loc["q"], db.k.view(-1)[1:], db.v, 2, 2, 64, 0.125, 1, out, lse, ws)  # misaligned K
+    meta.close()
+
+
+def test_ag_graph_capture_replays():
+    """The all-gather calls only launch kernels: captured into a HIP graph
+    (torch's stream capture) every replay equals the eager result bit for bit,
+    with eager work between replays."""
+    import torch
+    bt = synth.make_batch("ag-graph", 41, [700, 333, 64], [704, 336, 64], 4, 2, 128)
+    cp, r = 2, 1
+    scale = 1.0 / math.sqrt(bt.d)
+    db = H.DeviceBatch(bt)
+    meta, loc = H.local_inputs(db, cp, r)
+    ref = _run_ag(meta, db, loc, bt, scale, extra_rows=0)
+    torch.cuda.synchronize()
+    t_alloc, T = loc["t_alloc"], bt.total_rows
+    out = torch.zeros_like(ref[0])
+    lse = torch.zeros_like(ref[1])
+    dq = torch.zeros_like(ref[2])
+    dk = torch.zeros((T, bt.hkv, bt.d), dtype=torch.bfloat16, device="cuda")
+    dv = torch.zeros_like(dk)
+    wsf = torch.empty(api.cp_attn_ag_workspace_bytes(meta, bt.hq, bt.hkv, bt.d, 0), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(api.cp_attn_ag_workspace_bytes(meta, bt.hq, bt.hkv, bt.d, 1), dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            api.cp_attn_ag_fwd(meta, loc["q"], db.k, db.v, bt.hq, bt.hkv, bt.d, scale, 1, out, lse, wsf, stream=s)
+            api.cp_attn_ag_bwd(meta, loc["q"], db.k, db.v, out, lse, loc["do"], bt.hq, bt.hkv, bt.d, scale, 1, dq, dk,
+                               dv, wsb, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    tl = loc["t_local"]
+    for rep in range(3):
+        for t in (out, lse, dq, dk, dv):
+            t.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[:tl].view(torch.int16), ref[0][:tl].view(torch.int16)), rep
+        assert torch.equal(lse[:, :tl], ref[1][:, :tl]), rep
+        assert torch.equal(dq.view(torch.int16), ref[2].view(torch.int16)), rep
+        assert torch.equal(dk.view(torch.int16), ref[3].view(torch.int16)), rep
+        assert torch.equal(dv.view(torch.int16), ref[4].view(torch.int16)), rep
+        H.log(f"[ag graph] replay {rep} matches")
+    del g
     meta.close()
