@@ -1,6 +1,7 @@
 // Optional per-kernel timing with HIP events on each launch's own stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <string>
@@ -15,7 +16,7 @@ struct Rec {
   const char* name;
   hipEvent_t a, b;
 };
-bool g_on = false;
+std::atomic<bool> g_on{false};  // read by every launch, so atomic even though recording is single-threaded
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_free;
 

@@ -309,8 +309,10 @@ void cp_attn_graph_free(cp_attn_graph* g);
  * enabled, every kernel launched by cp_attn_fwd / cp_attn_bwd is bracketed by
  * a pair of HIP events recorded on its launch stream (so the timing includes
  * nothing but that stream's work between the two records). Launches made
- * while their stream is being captured into a graph are not recorded. Not thread-safe; meant for one benchmarking
- * thread.
+ * while their stream is being captured into a graph are not recorded.
+ * Recording is not thread-safe: enable it only while a single thread calls
+ * the library (a benchmarking thread); with recording off, calls from any
+ * number of threads are unaffected.
  * cp_attn_timing_enable(1) clears earlier records and starts recording;
  * cp_attn_timing_enable(0) stops recording.
  * cp_attn_timing_read waits for the recorded events and fills up to `max`
