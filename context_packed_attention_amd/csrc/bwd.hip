@@ -168,10 +168,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb)
           s[mb] = mfma32x32x16(lds_read_row<D, true>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
-          dp[mb] = mfma32x32x16(lds_read_row<D, true>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
-        }
       }
       if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
       if (p.causal && k0 + BN - 1 > wrow_lo) {
@@ -184,13 +182,24 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 #pragma unroll
           for (int j = 0; j < 16; ++j) s[mb][j] = (mb * 32 + (j >> 2) * 8 + (j & 3) <= rel) ? s[mb][j] : NEG_INF_F;
       }
+      // dP^T products with the probabilities computed beside them (4 per k
+      // step): the exponentials issue while the matrix unit works, instead
+      // of after both chains
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          dp[mb] = mfma32x32x16(lds_read_row<D, true>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
+#pragma unroll
+        for (int e = 0; e < 32 / NKK; ++e) {
+          const int j = kk * (32 / NKK) + e;
+          s[j >> 4][j & 15] = fast_exp2(fmaf(s[j >> 4][j & 15], c, -lse2));
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float pv = fast_exp2(fmaf(s[mb][j], c, -lse2));
-          s[mb][j] = pv * dp[mb][j];  // dS^T = P (dP - D)
-        }
+        for (int j = 0; j < 16; ++j) s[mb][j] *= dp[mb][j];  // dS^T = P (dP - D)
 #pragma unroll
       for (int kk2 = 0; kk2 < BN / 16; ++kk2) {
         const bf16x8_t ds = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
