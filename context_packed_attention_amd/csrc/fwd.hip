@@ -104,9 +104,9 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   };
 
   const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
-  // one key tile; masking runs only on a wavefront's last tiles (keys past
-  // the range, or at the causal step keys after its first row)
-  // first half of a key tile: scores, V fragments, softmax; P packed to bf16
+  // first half of a key tile: scores, V fragments, softmax, P packed to
+  // bf16; masking runs only on a wavefront's last tiles (keys past the
+  // range, or at the causal step keys after its first row)
   auto key_tile = [&](int kt, int buf, bool masked, bf16x8_t (&pb)[4], bf16x8_t (&vf)[4][NMD]) {
     const int k0 = kt * BN;
     f32x16_t s[2];
