@@ -43,6 +43,30 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _need(t, name: str, nbytes: int, dtype: str | None = None):
+    """Layout checks the C ABI cannot make (it sees only pointers): a torch
+    tensor argument must be a contiguous device tensor of the right element
+    type holding at least `nbytes`. Raw integer pointers pass unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: a device tensor is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and str(t.dtype) != "torch." + dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected torch.{dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: holds {have} bytes, the call needs {nbytes}")
+
+
+def _need_list(ts, name: str, count: int, nbytes: int, dtype: str | None = None):
+    if len(ts) != count:
+        raise ValueError(f"{name}: {len(ts)} tensors given, cp_size is {count}")
+    for i, t in enumerate(ts):
+        _need(t, f"{name}[{i}]", nbytes, dtype)
+
+
 def _ptr_array(ts):
     arr = (C.c_void_p * len(ts))()
     for i, t in enumerate(ts):
@@ -53,8 +77,9 @@ def _ptr_array(ts):
 class Meta:
     """Owns a cp_attn_meta handle (freed on close / garbage collection)."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, t_alloc: int = 0):
         self._h = C.c_void_p(handle)
+        self.t_alloc = int(t_alloc)  # rows of the rank's local tensors
         s = L.Summary()
         _check(L.load().cp_attn_meta_summary(self._h, C.byref(s)), "cp_attn_meta_summary")
         self.summary = s
@@ -72,6 +97,11 @@ class Meta:
     @property
     def cp(self) -> int:
         return int(self.summary.cp_size)
+
+    @property
+    def t_global(self) -> int:
+        """Rows of the whole packed batch, cu_seqlens_padded[B]."""
+        return self.t_local * self.cp
 
     def steps(self):
         s = self.summary
@@ -104,7 +134,7 @@ def cp_attn_rank_metadata(cu_seqlens, cu_seqlens_padded, cp_size: int, cp_rank: 
     rc = L.load().cp_attn_rank_metadata(_ptr(cu_seqlens), _ptr(cu_seqlens_padded), int(B), int(cp_size),
                                         int(cp_rank), int(pad_hint), int(t_alloc), _stream(stream), C.byref(h))
     _check(rc, "cp_attn_rank_metadata")
-    return Meta(h.value)
+    return Meta(h.value, int(t_alloc))
 
 
 def cp_attn_meta_export(meta: Meta) -> np.ndarray:
@@ -120,8 +150,26 @@ def cp_attn_workspace_bytes(meta: Meta, hq: int, hkv: int, d: int, pass_: int) -
     return int(L.load().cp_attn_workspace_bytes(meta.handle, hq, hkv, d, pass_))
 
 
+def _check_fwd(meta: Meta, q, k_shards, v_shards, hq, hkv, d, out, lse):
+    ta = meta.t_alloc
+    _need(q, "q", ta * hq * d * 2, "bfloat16")
+    _need_list(k_shards, "k_shards", meta.cp, ta * hkv * d * 2, "bfloat16")
+    _need_list(v_shards, "v_shards", meta.cp, ta * hkv * d * 2, "bfloat16")
+    _need(out, "out", ta * hq * d * 2, "bfloat16")
+    _need(lse, "lse", hq * ta * 4, "float32")
+
+
+def _check_bwd(meta: Meta, hq, hkv, d, dout, dq, dk_parts, dv_parts):
+    ta = meta.t_alloc
+    _need(dout, "dout", ta * hq * d * 2, "bfloat16")
+    _need(dq, "dq", ta * hq * d * 2, "bfloat16")
+    _need_list(dk_parts, "dk_parts", meta.cp, ta * hkv * d * 2, "bfloat16")
+    _need_list(dv_parts, "dv_parts", meta.cp, ta * hkv * d * 2, "bfloat16")
+
+
 def cp_attn_fwd(meta: Meta, q, k_shards, v_shards, hq: int, hkv: int, d: int, softmax_scale: float,
                 causal: int, out, lse, workspace, stream=None):
+    _check_fwd(meta, q, k_shards, v_shards, hq, hkv, d, out, lse)
     ks = _ptr_array(k_shards)
     vs = _ptr_array(v_shards)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -132,6 +180,8 @@ def cp_attn_fwd(meta: Meta, q, k_shards, v_shards, hq: int, hkv: int, d: int, so
 
 def cp_attn_bwd(meta: Meta, q, k_shards, v_shards, out, lse, dout, hq: int, hkv: int, d: int,
                 softmax_scale: float, causal: int, dq, dk_parts, dv_parts, workspace, stream=None):
+    _check_fwd(meta, q, k_shards, v_shards, hq, hkv, d, out, lse)
+    _check_bwd(meta, hq, hkv, d, dout, dq, dk_parts, dv_parts)
     ks = _ptr_array(k_shards)
     vs = _ptr_array(v_shards)
     dks = _ptr_array(dk_parts)
@@ -144,6 +194,8 @@ def cp_attn_bwd(meta: Meta, q, k_shards, v_shards, out, lse, dout, hq: int, hkv:
 
 
 def cp_attn_shard_gather(meta: Meta, shard: int, global_rows, local_rows, row_bytes: int, stream=None):
+    _need(global_rows, "global_rows", meta.t_global * row_bytes)
+    _need(local_rows, "local_rows", meta.t_local * row_bytes)
     rc = L.load().cp_attn_shard_gather(meta.handle, int(shard), _ptr(global_rows), _ptr(local_rows),
                                        int(row_bytes), _stream(stream))
     _check(rc, "cp_attn_shard_gather")
@@ -248,6 +300,9 @@ class Graph:
 def cp_attn_graph_capture(meta: Meta, passes: int, q, k_shards, v_shards, hq: int, hkv: int, d: int,
                           softmax_scale: float, causal: int, out, lse, dout=None, dq=None, dk_parts=(),
                           dv_parts=(), ws_fwd=None, ws_bwd=None) -> Graph:
+    _check_fwd(meta, q, k_shards, v_shards, hq, hkv, d, out, lse)
+    if int(passes) & 2:
+        _check_bwd(meta, hq, hkv, d, dout, dq, dk_parts, dv_parts)
     ks = _ptr_array(k_shards)
     vs = _ptr_array(v_shards)
     dks = _ptr_array(dk_parts) if dk_parts else None
@@ -268,6 +323,8 @@ def cp_attn_a2a_seq_to_head(meta: Meta, a2a_size: int, p2p_rank: int, heads: int
                             stream=None):
     """Group p2p_rank's all-to-all: ins[a] = CP rank p*A + a's local tensor
     (all heads), outs[a'] = head group a' of p2p rank p's local rows."""
+    _need_list(ins, "ins", a2a_size, meta.t_local * heads * head_bytes)
+    _need_list(outs, "outs", a2a_size, meta.t_local * heads * head_bytes)
     rc = L.load().cp_attn_a2a_seq_to_head(meta.handle, int(a2a_size), int(p2p_rank), int(heads), int(head_bytes),
                                           _ptr_array(ins), _ptr_array(outs), _stream(stream))
     _check(rc, "cp_attn_a2a_seq_to_head")
@@ -277,6 +334,8 @@ def cp_attn_a2a_head_to_seq(meta: Meta, a2a_size: int, p2p_rank: int, heads: int
                             stream=None):
     """The inverse all-to-all: ins[a'] = head group a' of p2p rank p's local
     rows, outs[a] = CP rank p*A + a's local tensor (all heads)."""
+    _need_list(ins, "ins", a2a_size, meta.t_local * heads * head_bytes)
+    _need_list(outs, "outs", a2a_size, meta.t_local * heads * head_bytes)
     rc = L.load().cp_attn_a2a_head_to_seq(meta.handle, int(a2a_size), int(p2p_rank), int(heads), int(head_bytes),
                                           _ptr_array(ins), _ptr_array(outs), _stream(stream))
     _check(rc, "cp_attn_a2a_head_to_seq")
@@ -290,6 +349,12 @@ def cp_attn_ag_fwd(meta: Meta, q, k_full, v_full, hq: int, hkv: int, d: int, sof
                    out, lse, workspace, stream=None):
     """All-gather share, forward: k_full / v_full are the gathered K / V in
     packed (cu_seqlens_padded) order."""
+    ta = meta.t_alloc
+    _need(q, "q", ta * hq * d * 2, "bfloat16")
+    _need(k_full, "k_full", meta.t_global * hkv * d * 2, "bfloat16")
+    _need(v_full, "v_full", meta.t_global * hkv * d * 2, "bfloat16")
+    _need(out, "out", ta * hq * d * 2, "bfloat16")
+    _need(lse, "lse", hq * ta * 4, "float32")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = L.load().cp_attn_ag_fwd(meta.handle, _ptr(q), _ptr(k_full), _ptr(v_full), hq, hkv, d, float(softmax_scale),
                                  int(causal), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
@@ -300,6 +365,12 @@ def cp_attn_ag_bwd(meta: Meta, q, k_full, v_full, out, lse, dout, hq: int, hkv: 
                    causal: int, dq, dk_full, dv_full, workspace, stream=None):
     """All-gather share, backward: dk_full / dv_full receive this rank's
     contribution to every gathered key row."""
+    ta = meta.t_alloc
+    for t, nm in ((q, "q"), (out, "out"), (dout, "dout"), (dq, "dq")):
+        _need(t, nm, ta * hq * d * 2, "bfloat16")
+    for t, nm in ((k_full, "k_full"), (v_full, "v_full"), (dk_full, "dk_full"), (dv_full, "dv_full")):
+        _need(t, nm, meta.t_global * hkv * d * 2, "bfloat16")
+    _need(lse, "lse", hq * ta * 4, "float32")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = L.load().cp_attn_ag_bwd(meta.handle, _ptr(q), _ptr(k_full), _ptr(v_full), _ptr(out), _ptr(lse), _ptr(dout),
                                  hq, hkv, d, float(softmax_scale), int(causal), _ptr(dq), _ptr(dk_full),

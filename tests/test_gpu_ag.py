@@ -96,8 +96,12 @@ def test_ag_argument_errors():
         api.cp_attn_ag_fwd(meta, loc["q"], db.k, db.v, 2, 2, 64, 0.125, 1, out, lse, small)
     assert e.value.status == 4  # workspace too small
     ws = torch.empty(api.cp_attn_ag_workspace_bytes(meta, 2, 2, 64, 0), dtype=torch.uint8, device="cuda")
+    n = db.k.numel()
+    buf = torch.empty(n + 8, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(api.CpAttnError):
-        api.cp_attn_ag_fwd(meta, loc["q"], db.k.view(-1)[1:], db.v, 2, 2, 64, 0.125, 1, out, lse, ws)  # misaligned K
+        api.cp_attn_ag_fwd(meta, loc["q"], buf[1:1 + n], db.v, 2, 2, 64, 0.125, 1, out, lse, ws)  # misaligned K
+    with pytest.raises(ValueError):
+        api.cp_attn_ag_fwd(meta, loc["q"], db.k[:-1], db.v, 2, 2, 64, 0.125, 1, out, lse, ws)  # K too short
     meta.close()
 
 
