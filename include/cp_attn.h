@@ -130,7 +130,10 @@ cp_attn_status cp_attn_meta_export(const cp_attn_meta* m, int32_t* host_buf, siz
 /* Release the handle (synchronises the device it was built on). NULL is a no-op. */
 void cp_attn_meta_free(cp_attn_meta* m);
 
-/* Workspace bytes needed by cp_attn_fwd (pass 0) or cp_attn_bwd (pass 1). */
+/* Workspace bytes needed by cp_attn_fwd (pass 0) or cp_attn_bwd (pass 1);
+ * 0 for a NULL handle or non-positive sizes. The forward's figure depends on
+ * the launch plan (see cp_attn_fwd), so take it from this call rather than a
+ * formula. */
 size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, int32_t d, int32_t pass);
 
 /*
@@ -138,7 +141,12 @@ size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, i
  * rows attend to the step's key rows of shard s = (rank - i) mod CP (one
  * flash-style MFMA kernel per step, causal on local rows at step 0 only),
  * and the per-step partial outputs are folded through their log-sum-exp.
- * [I1] the P2P ring; [I2] "Describe the bug": per-step metadata.
+ * [I1] the P2P ring; [I2] "Describe the bug": per-step metadata. When every
+ * step's launch is short (under four waves of two blocks per compute unit)
+ * the steps run concurrently on side streams forked from `stream` by events
+ * and joined back before one merge of all partials (the workspace then holds
+ * one partial per step); otherwise they run in order on `stream`. Either way
+ * the call is ordered on `stream` alone.
  *
  *  q                  bf16 [t_alloc, hq, d]: this rank's query rows
  *  k_shards, v_shards HOST arrays of CP device pointers, bf16 [t_alloc, hkv, d];
