@@ -175,6 +175,9 @@ cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, const void* con
  * THD gradient tail zeroing ([I2] "Describe the bug" and "Expected
  * behavior"): rows [T_local, t_alloc) of dq and of every part are zeroed by
  * one extra launch, made only when the metadata shows such a tail exists.
+ * When the steps' launches are short the dK/dV chain runs on a side stream
+ * forked from `stream` beside the dQ chain and is joined back before the call
+ * returns its work to `stream`.
  *
  *  q, k_shards, v_shards, hq, hkv, d, softmax_scale, causal: as cp_attn_fwd
  *  out, lse           the forward's outputs
