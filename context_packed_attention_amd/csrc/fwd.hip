@@ -33,9 +33,19 @@ struct FwdParams {
   long long ld_q, ld_kv;  // elements per row
   float scale, c_log2;    // softmax scale, scale * log2(e)
   int causal;
-  float* o;               // fp32 [rows, hq, D]
+  float* o;               // fp32 [rows, hq, D]: the step's partial, or the running accumulator
   float* lse;             // fp32 [hq, ld_lse]
   long long ld_o, ld_lse;
+  // epilogue: 0 = write the step's normalised partial (o, lse); 1 = fold it
+  // into the accumulator (o, lse) through the log-sum-exp; 2 = fold it and
+  // write the result as the bf16 output and final LSE instead. acc_first /
+  // acc_second: whether the accumulator already holds rows of the first /
+  // second chunk (earlier steps covered them).
+  int mode, acc_first, acc_second;
+  const int32_t* rowflags;
+  uint16_t* out;
+  float* lse_out;
+  long long ld_lse_out;
 };
 
 // One block = NWAVES wavefronts (FWD_BM query rows) of one head; each wavefront owns
@@ -212,78 +222,76 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       inv = 0.f;
       lse = NEG_INF_F;
     }
-    float* orow = p.o + (long long)(qs + qrow) * p.ld_o + head * D + g * 4;
+    const int t = qs + qrow;  // local row
+    float* orow = p.o + (long long)t * p.ld_o + head * D + g * 4;
+    float* lrow = p.lse + (long long)head * p.ld_lse + t;
+    if (p.mode == 0) {
 #pragma unroll
-    for (int md = 0; md < NMD; ++md)
+      for (int md = 0; md < NMD; ++md)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float4 val = make_float4(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
-                                 o[md][4 * jj + 3] * inv);
-        *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
+        for (int jj = 0; jj < 4; ++jj) {
+          float4 val = make_float4(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
+                                   o[md][4 * jj + 3] * inv);
+          *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
+        }
+      if (g == 0) *lrow = lse;
+    } else {
+      // fold into the accumulator: out = (e^(la-m) out_a + e^(lb-m) out_b) /
+      // (e^(la-m) + e^(lb-m)), lse = m + log of that sum, m = max(la, lb)
+      const bool has = (p.rowflags[t] & RF_SECOND) ? p.acc_second : p.acc_first;
+      const float la = has ? *lrow : NEG_INF_F;
+      const float mx = fmaxf(la, lse);
+      float wa = 0.f, wb = 0.f, lm = NEG_INF_F;
+      if (mx != NEG_INF_F) {
+        wa = __expf(la - mx);
+        wb = __expf(lse - mx);
+        const float ssum = wa + wb;
+        lm = mx + __logf(ssum);
+        const float r = 1.f / ssum;
+        wa *= r;
+        wb *= r * inv;
       }
-    if (g == 0) p.lse[(long long)head * p.ld_lse + qs + qrow] = lse;
+      uint16_t* out_row = p.out + (long long)t * p.ld_o + head * D + g * 4;
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (has) a = *reinterpret_cast<const float4*>(orow + md * 32 + jj * 8);
+          const float4 val = make_float4(wa * a.x + wb * o[md][4 * jj], wa * a.y + wb * o[md][4 * jj + 1],
+                                         wa * a.z + wb * o[md][4 * jj + 2], wa * a.w + wb * o[md][4 * jj + 3]);
+          if (p.mode == 1) {
+            *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
+          } else {
+            uint2 pk;
+            pk.x = pack2_bf16(val.x, val.y);
+            pk.y = pack2_bf16(val.z, val.w);
+            *reinterpret_cast<uint2*>(out_row + md * 32 + jj * 8) = pk;
+          }
+        }
+      if (g == 0) {
+        if (p.mode == 1)
+          *lrow = lm;
+        else
+          p.lse_out[(long long)head * p.ld_lse_out + t] = lm;
+      }
+    }
   }
 }
 
-// Log-sum-exp merge of a step partial into the accumulator (one wavefront
-// covers 64 x 4 consecutive fp32 of a row, i.e. whole heads). `kind` is the
-// partial's step kind (-1: no partial, only the final conversion); rows a
-// step does not cover keep the accumulator. With `final`, every local row is
-// written to the bf16 output: merged values for valid rows, 0 (and lse
-// -inf) for padding rows.
-__global__ void __launch_bounds__(256) lse_merge_kernel(float* __restrict__ acc_o, float* __restrict__ acc_lse,
-                                                        const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_lse,
-                                                        const int32_t* __restrict__ rowflags, int kind, int final_pass,
-                                                        uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                                                        int t_local, int hq, int d, long long ld_lse_out) {
-  const long long q4_per_row = (long long)hq * d / 4;
-  const long long n = (long long)t_local * q4_per_row;
+// Padding rows of the final output: out 0, LSE -inf (every valid row is
+// written by the last ring step's epilogue).
+__global__ void __launch_bounds__(256) pad_rows_kernel(const int32_t* __restrict__ rowflags, uint16_t* __restrict__ out,
+                                                       float* __restrict__ lse_out, int t_local, int hq, int d,
+                                                       long long ld_lse_out) {
+  const long long u_per_row = (long long)hq * d / 8;  // 16-byte units
+  const long long n = (long long)t_local * u_per_row;
   for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
-    const int t = (int)(e / q4_per_row);
-    const int off = (int)(e - (long long)t * q4_per_row) * 4;
-    const int h = off / d;
-    const int f = rowflags[t];
-    const bool valid = f & RF_VALID;
-    const bool covered = kind >= 0 && valid && (kind != 2 || (f & RF_SECOND));
-    if (!covered && !final_pass) continue;
-    float4 oa = make_float4(0.f, 0.f, 0.f, 0.f);
-    float la = NEG_INF_F;
-    if (valid) {
-      oa = *reinterpret_cast<const float4*>(acc_o + (long long)t * hq * d + off);
-      la = acc_lse[(long long)h * t_local + t];
-    }
-    if (covered) {
-      const float4 ob = *reinterpret_cast<const float4*>(part_o + (long long)t * hq * d + off);
-      const float lb = part_lse[(long long)h * t_local + t];
-      const float m = fmaxf(la, lb);
-      float wa = 0.f, wb = 0.f, l = NEG_INF_F;
-      if (m != NEG_INF_F) {
-        wa = __expf(la - m);
-        wb = __expf(lb - m);
-        const float ssum = wa + wb;
-        l = m + __logf(ssum);
-        const float inv = 1.f / ssum;
-        wa *= inv;
-        wb *= inv;
-      }
-      oa = make_float4(wa * oa.x + wb * ob.x, wa * oa.y + wb * ob.y, wa * oa.z + wb * ob.z, wa * oa.w + wb * ob.w);
-      la = l;
-      if (!final_pass) {
-        *reinterpret_cast<float4*>(acc_o + (long long)t * hq * d + off) = oa;
-        // every lane of this (row, head) read acc_lse above: the (row, head)
-        // group is D/4 <= 32 consecutive lanes of one wavefront, whose loads
-        // complete before this store issues
-        if ((off % d) == 0) acc_lse[(long long)h * t_local + t] = l;
-      }
-    }
-    if (final_pass) {
-      uint2 pk;
-      pk.x = pack2_bf16(oa.x, oa.y);
-      pk.y = pack2_bf16(oa.z, oa.w);
-      *reinterpret_cast<uint2*>(out + (long long)t * hq * d + off) = pk;
-      if ((off % d) == 0) lse_out[(long long)h * ld_lse_out + t] = valid ? la : NEG_INF_F;
-    }
+    const int t = (int)(e / u_per_row);
+    if (rowflags[t] & RF_VALID) continue;
+    const int u = (int)(e - (long long)t * u_per_row);
+    reinterpret_cast<uint4*>(out + (long long)t * hq * d)[u] = make_uint4(0, 0, 0, 0);
+    if (u < hq) lse_out[(long long)u * ld_lse_out + t] = NEG_INF_F;
   }
 }
 
@@ -384,8 +392,8 @@ extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int
   const size_t o = tl * hq * d * sizeof(float);
   const size_t l = ((tl * hq * sizeof(float)) + 255) & ~size_t(255);
   const size_t o_al = (o + 255) & ~size_t(255);
-  if (pass == 0)  // accumulator + step partial (out, lse), or one partial per step when the steps run concurrently
-    return (fwd_forks(m, hq) ? (size_t)m->cp : 2) * (o_al + l);
+  if (pass == 0)  // the running accumulator (out, lse), or one partial per step when the steps run concurrently
+    return (fwd_forks(m, hq) ? (size_t)m->cp : 1) * (o_al + l);
   return o_al + 2 * l;                     // dq accumulator + per-row lse and -D = -rowsum(dO * O)
 }
 
@@ -428,10 +436,6 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
   const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);
   char* ws = (char*)workspace;
-  float* acc_o = (float*)ws;
-  float* part_o = (float*)(ws + o_al);
-  float* acc_l = (float*)(ws + 2 * o_al);
-  float* part_l = (float*)(ws + 2 * o_al + l_al);
   const int32_t* rowflags = m->d_tab + m->lay.rowflags;
 
   FwdParams base{};
@@ -444,6 +448,10 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   base.c_log2 = softmax_scale * LOG2E_F;
   base.ld_o = (long long)hq * d;
   base.ld_lse = tl;
+  base.rowflags = rowflags;
+  base.out = (uint16_t*)out;
+  base.lse_out = lse;
+  base.ld_lse_out = (long long)m->t_alloc;
   const long long n4 = (long long)tl * hq * d / 4;
   if (fwd_forks(m, hq)) {
     // step i into partial i, the steps spread over the caller's stream and
@@ -474,31 +482,38 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
     timing_end(st);
     return hip_check(hipGetLastError(), "lse_merge launch");
   }
-  for (int i = 0; i < m->cp; ++i) {
-    const int s = m->sum.step_src[i];
+  // In order: each step folds its partial into the accumulator in its own
+  // epilogue. The steps are independent on one device, so the second-chunk
+  // steps (kind 2) run first, then the kind-1 steps, and the causal step,
+  // which covers every valid row of both chunks, runs last and writes the
+  // bf16 output and the final LSE.
+  int order[CP_ATTN_MAX_CP], n_order = 0;
+  for (int want : {2, 1, 0})
+    for (int i = 0; i < m->cp; ++i)
+      if (m->sum.step_kind[i] == want) order[n_order++] = i;
+  bool acc_first = false, acc_second = false;
+  for (int k = 0; k < n_order; ++k) {
+    const int i = order[k];
+    const int kind = m->sum.step_kind[i];
     FwdParams p = base;
-    p.k = (const uint16_t*)k_shards[s];
-    p.v = (const uint16_t*)v_shards[s];
-    p.o = (i == 0) ? acc_o : part_o;
-    p.lse = (i == 0) ? acc_l : part_l;
+    p.k = (const uint16_t*)k_shards[m->sum.step_src[i]];
+    p.v = (const uint16_t*)v_shards[m->sum.step_src[i]];
+    p.o = (float*)ws;
+    p.lse = (float*)(ws + o_al);
+    p.mode = (k == n_order - 1) ? 2 : 1;
+    p.acc_first = acc_first;
+    p.acc_second = acc_second;
     rc = launch_fwd_step(m, i, p, d, (int)m->sum.tiles_fwd[i], st);
     if (rc != CP_ATTN_OK) return rc;
-    if (i >= 1) {
-      timing_begin(st, "lse_merge");
-      hipLaunchKernelGGL(lse_merge_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, acc_o, acc_l, part_o,
-                         part_l, rowflags, m->sum.step_kind[i], (i == m->cp - 1) ? 1 : 0, (uint16_t*)out, lse, tl, hq,
-                         d, (long long)m->t_alloc);
-      timing_end(st);
-      rc = hip_check(hipGetLastError(), "lse_merge launch");
-      if (rc != CP_ATTN_OK) return rc;
-    }
+    acc_second = true;
+    if (kind != 2) acc_first = true;
   }
-  if (m->cp == 1) {
-    timing_begin(st, "lse_merge");
-    hipLaunchKernelGGL(lse_merge_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, acc_o, acc_l, part_o, part_l,
-                       rowflags, -1, 1, (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
+  if (m->sum.valid_rows < tl) {
+    timing_begin(st, "pad_rows");
+    hipLaunchKernelGGL(pad_rows_kernel, dim3(stream_blocks((long long)tl * hq * d / 8, 256)), dim3(256), 0, st,
+                       rowflags, (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
     timing_end(st);
-    rc = hip_check(hipGetLastError(), "lse_merge launch");
+    rc = hip_check(hipGetLastError(), "pad_rows launch");
   }
   return rc;
 }
