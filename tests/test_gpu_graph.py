@@ -23,11 +23,19 @@ def _same(name, a, b):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"{name} differs from the eager result"
 
 
-@pytest.mark.parametrize("cfg,rank,tail", [(2, 1, 0), (3, 0, 0), (1, 1, 37)])
+# the padded pack of test_gpu_inorder: long enough for the in-order launch plan
+INORDER = ([3000, 1500, 3800, 5], [3008, 1600, 3804, 8], 2, 64, 8, 64)
+
+
+@pytest.mark.parametrize("cfg,rank,tail", [(2, 1, 0), (3, 0, 0), (1, 1, 37), ("inorder", 1, 0)])
 def test_graph_replays_match_eager(cfg, rank, tail):
     import torch
-    bt, w = synth.make_workload(cfg)
-    cp = w["cp"]
+    if cfg == "inorder":
+        L, P, cp, hq, hkv, d = INORDER
+        bt = synth.make_batch("inorder-padded", 17, L, P, hq, hkv, d)
+    else:
+        bt, w = synth.make_workload(cfg)
+        cp = w["cp"]
     H.log(f"[graph] cfg{cfg} rank {rank} tail {tail}")
     db = H.DeviceBatch(bt)
     meta, loc = H.local_inputs(db, cp, rank, tail=tail)
