@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4,
                     help="1..5: tiny / 16K pack / padded 16K pack / 131072-token GQA / 64K hierarchical pack")
-    ap.add_argument("--cpu-sample-stride", type=int, default=256,
+    ap.add_argument("--cpu-sample-stride", type=int, default=128,
                     help="oracle baseline: every Nth query row of the share (0 = skip the baseline)")
     ap.add_argument("--a2a", action="store_true",
                     help="only time the hierarchical front end's all-to-all (sequence split -> head split and back) "
@@ -83,6 +83,10 @@ def parse():
     ap.add_argument("--all-gather", action="store_true",
                     help="time the all-gather share of the selected workload instead (gathered K/V in, the rank's "
                          "contribution to every gathered dK/dV row out) and exit")
+    ap.add_argument("--pad-hint-abba", action="store_true",
+                    help="only run the padding-decision A/B on the 16K pack (cu_seqlens_padded a distinct, "
+                         "value-equal copy): steps with pad_hint -1 and 0 alternate in A B B A blocks of --steps "
+                         "steps, repeated three times; print both step times and launch sequences and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and exit "
                          "(the known-size reference for the HBM byte counters)")
@@ -278,6 +282,96 @@ def ag_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def abba_bench(args):
+    """The padding decision's cost, after the pages' own experiment ("[PyTorch]
+    [Attention] THD P2P context-parallel regression when padded cu_seqlens are
+    value-equal but not object-identical", Describe the bug: the same batch run
+    with value-equal cu_seqlens_padded as a copy and as the same object took
+    different paths and times). Here the decision is made on the device from
+    values: pad_hint -1 (decide from the values) and 0 (the caller asserts no
+    padding) must give the same launch sequence and the same step time within
+    noise. Steps alternate in A B B A blocks so a drift of the clock or the
+    box's load falls on both sides alike."""
+    import numpy as np
+    import torch
+    from context_packed_attention_amd import api, synth
+    w = synth.workload(2)
+    rank = w["ranks"][-1]
+    batch, _ = synth.make_workload(2)
+    cp, hq, hkv, d = w["cp"], w["hq"], w["hkv"], w["d"]
+    scale = 1.0 / math.sqrt(d)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    cu = torch.tensor(batch.cu, dtype=torch.int32, device="cuda")
+    cup = torch.tensor(batch.cup, dtype=torch.int32, device="cuda")  # distinct tensor, equal values
+    t_alloc = int(batch.cup[-1]) // cp
+    meta = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc)
+    gq, gk, gv, gdo = (dev_bf16(x) for x in (batch.q, batch.k, batch.v, batch.do))
+
+    def gather(src, h, s):
+        dst = torch.empty((t_alloc, h, d), dtype=torch.bfloat16, device="cuda")
+        api.cp_attn_shard_gather(meta, s, src, dst, h * d * 2)
+        return dst
+
+    q, do = gather(gq, hq, rank), gather(gdo, hq, rank)
+    ks = [gather(gk, hkv, s) for s in range(cp)]
+    vs = [gather(gv, hkv, s) for s in range(cp)]
+    out = torch.empty_like(q)
+    lse = torch.empty((hq, t_alloc), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dks = [torch.empty_like(x) for x in ks]
+    dvs = [torch.empty_like(x) for x in vs]
+    ws_f = torch.empty(api.cp_attn_workspace_bytes(meta, hq, hkv, d, 0), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(api.cp_attn_workspace_bytes(meta, hq, hkv, d, 1), dtype=torch.uint8, device="cuda")
+    pairs = sum(api.step_pairs(meta))
+    meta.close()
+    stream = torch.cuda.current_stream()
+
+    def block(hint, n, record):
+        held = []
+        api.cp_attn_timing_enable(record)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            m = api.cp_attn_rank_metadata(cu, cup, cp, rank, hint, t_alloc, stream=stream)
+            api.cp_attn_fwd(m, q, ks, vs, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream)
+            api.cp_attn_bwd(m, q, ks, vs, out, lse, do, hq, hkv, d, scale, 1, dq, dks, dvs, ws_b, stream=stream)
+            held.append(m)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) * 1e3 / n
+        api.cp_attn_timing_enable(False)
+        launches = {k: v[1] / n for k, v in api.cp_attn_timing_read().items()} if record else None
+        for m in held:
+            m.close()
+        return dt, launches
+
+    hints = {"A": -1, "B": 0}
+    for h in hints.values():
+        block(h, args.warmup, False)
+    launches = {k: block(h, 1, True)[1] for k, h in hints.items()}
+    times = {"A": [], "B": []}
+    order = "ABBA" * 3
+    for k in order:
+        times[k].append(block(hints[k], args.steps, False)[0])
+    ma, mb = float(np.mean(times["A"])), float(np.mean(times["B"]))
+    spread = float(np.std(times["A"] + times["B"]) / np.mean(times["A"] + times["B"]))
+    line = {
+        "metric": "padding decision A/B on the 16K pack: ms per step with pad_hint -1 vs 0 (1 MI355X)",
+        "value": round(ma, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ma, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO)",
+        "config": {"workload": w["name"], "cp_size": cp, "cp_rank": rank, "hq": hq, "hkv": hkv, "head_dim": d,
+                   "pairs": pairs, "order": order, "steps_per_block": args.steps,
+                   "cu_seqlens_padded": "distinct tensor, value-equal"},
+        "hint_auto_ms": round(ma, 4), "hint_zero_ms": round(mb, 4), "ratio": round(ma / mb, 4),
+        "block_spread": round(spread, 4), "blocks_ms": {k: [round(x, 4) for x in v] for k, v in times.items()},
+        "same_launches": launches["A"] == launches["B"], "launches_per_step": launches["A"],
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -302,6 +396,9 @@ def main():
         return
     if args.all_gather:
         ag_bench(args)
+        return
+    if args.pad_hint_abba:
+        abba_bench(args)
         return
     w = synth.workload(args.workload)
     rank = w["ranks"][-1] if args.workload != 1 else 0
@@ -435,6 +532,16 @@ def main():
     graph.close()
     gmeta.close()
 
+    # attainable matrix-unit rate on this device: the library's calibration
+    # kernel (nothing but independent MFMA chains), best of three launches
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    probes = [api.cp_attn_mfma_probe(100000, sink, stream=stream) for _ in range(3)]
+    attainable = max(tf for _, tf in probes)
+    log(f"[bench] matrix-unit calibration: {attainable:.1f} TFLOP/s attainable")
+    if roof.get("bound") == "mfma":
+        roof["attainable_peak"] = round(attainable, 1)
+        roof["frac_of_attainable"] = round(roof["achieved"] / attainable, 4)
+
     cpu = None
     if args.cpu_sample_stride > 0:
         log("[bench] oracle CPU baseline")
@@ -446,6 +553,7 @@ def main():
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "pct_of_attainable": round(100.0 * tflops / attainable, 2),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -463,6 +571,9 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "graph": graph_info,
+        "mfma_calibration": {"attainable_tflops": round(attainable, 1),
+                             "launch_ms": [round(m, 3) for m, _ in probes],
+                             "kernel": "independent v_mfma_f32_32x32x16_bf16 chains, 8 per SIMD, no memory traffic"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -24,7 +24,7 @@ EXPORTED = [
     "cp_attn_timing_enable", "cp_attn_timing_read",
     "cp_attn_graph_capture", "cp_attn_graph_launch", "cp_attn_graph_kernels", "cp_attn_graph_free",
     "cp_attn_a2a_seq_to_head", "cp_attn_a2a_head_to_seq",
-    "cp_attn_ag_workspace_bytes", "cp_attn_ag_fwd", "cp_attn_ag_bwd",
+    "cp_attn_ag_workspace_bytes", "cp_attn_ag_fwd", "cp_attn_ag_bwd", "cp_attn_mfma_probe",
 ]
 
 
@@ -94,6 +94,8 @@ def load(path: str | None = None) -> C.CDLL:
     lib.cp_attn_ag_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, C.c_float, i32, vp, vp, vp, vp,
                                    C.c_size_t, vp]
     lib.cp_attn_ag_bwd.restype = st
+    lib.cp_attn_mfma_probe.argtypes = [i32, vp, vp, C.POINTER(C.c_double), C.POINTER(C.c_double)]
+    lib.cp_attn_mfma_probe.restype = st
     lib.cp_attn_last_error.argtypes = []
     lib.cp_attn_last_error.restype = C.c_char_p
     _lib = lib

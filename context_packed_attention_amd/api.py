@@ -209,6 +209,18 @@ def cp_attn_timing_enable(on: bool):
     _check(L.load().cp_attn_timing_enable(1 if on else 0), "cp_attn_timing_enable")
 
 
+def cp_attn_mfma_probe(iters: int, sink, stream=None) -> tuple:
+    """(ms, TFLOP/s) of one launch of the library's matrix-unit calibration
+    kernel; sink: a device float32 tensor of at least one element."""
+    import torch
+    if not isinstance(sink, torch.Tensor) or not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < 1:
+        raise ValueError("sink must be a float32 CUDA tensor of at least one element")
+    ms, tf = C.c_double(), C.c_double()
+    rc = L.load().cp_attn_mfma_probe(int(iters), sink.data_ptr(), _stream(stream), C.byref(ms), C.byref(tf))
+    _check(rc, "cp_attn_mfma_probe")
+    return float(ms.value), float(tf.value)
+
+
 def cp_attn_timing_read(max_kernels: int = 32) -> dict:
     """{kernel name: (total ms, launches)} of the launches recorded since enabling."""
     name_len = 64

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "kern_common.h"
 
 namespace cpattn {
 
@@ -59,9 +60,66 @@ void timing_end(hipStream_t st) {
   if (r.b) (void)hipEventRecord(r.b, st);
 }
 
+// Matrix-unit calibration: four independent v_mfma_f32_32x32x16_bf16 chains
+// per wavefront on register operands (no memory traffic in the loop), two
+// 4-wavefront blocks per compute unit, so every SIMD keeps eight chains in
+// flight. The sum is stored only if it hits an impossible value, which keeps
+// the chains live without writing anything.
+__global__ void __launch_bounds__(256, 2) mfma_probe_kernel(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)((float)((lane + e) & 7) * 1e-3f);
+    b[e] = (__bf16)((float)((lane * 3 + e) & 7) * 1e-3f);
+  }
+  f32x16_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = zero16();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = mfma32x32x16(a, b, acc[c]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[c][j];
+  if (s == -1234.5f) sink[0] = s;
+}
+
 }  // namespace cpattn
 
 using namespace cpattn;
+
+extern "C" cp_attn_status cp_attn_mfma_probe(int32_t iters, float* sink, void* stream, double* ms, double* tflops) {
+  set_error("");
+  if (iters <= 0 || !sink || !ms || !tflops) return fail(CP_ATTN_ERR_INVALID_ARG, "mfma probe: bad argument");
+  int dev = 0;
+  cp_attn_status rc;
+  if ((rc = hip_check(hipGetDevice(&dev), "hipGetDevice")) != CP_ATTN_OK) return rc;
+  const int blocks = 2 * cu_count(dev);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if ((rc = hip_check(hipEventCreate(&e0), "hipEventCreate")) != CP_ATTN_OK) return rc;
+  if ((rc = hip_check(hipEventCreate(&e1), "hipEventCreate")) != CP_ATTN_OK) {
+    (void)hipEventDestroy(e0);
+    return rc;
+  }
+  (void)hipEventRecord(e0, st);
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, st, iters, sink);
+  rc = hip_check(hipGetLastError(), "mfma probe launch");
+  (void)hipEventRecord(e1, st);
+  float t = 0.f;
+  if (rc == CP_ATTN_OK) rc = hip_check(hipEventSynchronize(e1), "mfma probe sync");
+  if (rc == CP_ATTN_OK) rc = hip_check(hipEventElapsedTime(&t, e0, e1), "mfma probe timing");
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != CP_ATTN_OK) return rc;
+  *ms = t;
+  *tflops = (double)blocks * 4 * 4 * (double)iters * (32.0 * 32 * 16 * 2) / (t * 1e-3) / 1e12;
+  return CP_ATTN_OK;
+}
 
 extern "C" cp_attn_status cp_attn_timing_enable(int32_t on) {
   if (on) recycle_all();

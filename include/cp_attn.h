@@ -335,6 +335,19 @@ void cp_attn_graph_free(cp_attn_graph* g);
 cp_attn_status cp_attn_timing_enable(int32_t on);
 int32_t cp_attn_timing_read(char* names, int32_t name_len, double* total_ms, int64_t* launches, int32_t max);
 
+/*
+ * Attainable bf16 matrix-unit rate (measurement tooling, not on the numerical
+ * path): one launch of independent v_mfma_f32_32x32x16_bf16 chains on register
+ * operands, two 256-thread blocks per compute unit of the current device,
+ * `iters` products per chain, timed with HIP events on `stream` (the call
+ * waits for it). Reports the launch's milliseconds and its dense bf16
+ * TFLOP/s, the rate the attention kernels can reach at the clock the device
+ * holds under matrix load. `sink`: device float, written only in a case that
+ * cannot occur (keeps the products live). Errors: CP_ATTN_ERR_INVALID_ARG for
+ * iters <= 0 or a NULL pointer, CP_ATTN_ERR_HIP for a failed launch.
+ */
+cp_attn_status cp_attn_mfma_probe(int32_t iters, float* sink, void* stream, double* ms, double* tflops);
+
 /* Thread-local description of the last failure ("" if none). */
 const char* cp_attn_last_error(void);
 

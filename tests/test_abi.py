@@ -58,6 +58,9 @@ def test_host_argument_checks_without_gpu():
     assert lib.cp_attn_a2a_seq_to_head(None, 2, 0, 4, 256, None, None, None) == _lib.ERR_INVALID_ARG
     assert lib.cp_attn_a2a_head_to_seq(None, 2, 0, 4, 256, None, None, None) == _lib.ERR_INVALID_ARG
     assert lib.cp_attn_ag_workspace_bytes(None, 1, 1, 128, 0) == 0
+    ms, tf = C.c_double(), C.c_double()
+    assert lib.cp_attn_mfma_probe(0, dummy, None, C.byref(ms), C.byref(tf)) == _lib.ERR_INVALID_ARG
+    assert lib.cp_attn_mfma_probe(10, None, None, C.byref(ms), C.byref(tf)) == _lib.ERR_INVALID_ARG
     assert lib.cp_attn_ag_fwd(None, None, None, None, 1, 1, 128, 1.0, 1, None, None, None, 0, None) == \
         _lib.ERR_INVALID_ARG
     assert lib.cp_attn_ag_bwd(None, None, None, None, None, None, None, 1, 1, 128, 1.0, 1, None, None, None, None, 0,

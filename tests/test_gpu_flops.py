@@ -1,5 +1,6 @@
 """The pair count the benchmark derives from the device tables equals the
-oracle's count of causal pairs of the rank's share."""
+oracle's count of causal pairs of the rank's share; the matrix-unit
+calibration the benchmark reports beside it gives a plausible rate."""
 import numpy as np
 import pytest
 
@@ -23,3 +24,18 @@ def test_step_pairs_match_oracle(cfg):
         ref = O.flops_share(cu, cup, w["cp"], r, w["hq"], w["d"])["pairs"]
         assert got == ref, (cfg, r, got, ref)
         m.close()
+
+
+def test_mfma_calibration_within_the_published_peak():
+    # the matrix-unit calibration kernel: a positive rate that cannot exceed
+    # the device's published dense bf16 peak (2.5 PFLOP/s) by more than timing
+    # noise, and a doubled chain length takes about twice as long
+    import torch
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    api.cp_attn_mfma_probe(1000, sink)  # warm up
+    ms1, tf1 = api.cp_attn_mfma_probe(20000, sink)
+    ms2, tf2 = api.cp_attn_mfma_probe(40000, sink)
+    H.log(f"[mfma probe] {tf1:.1f} / {tf2:.1f} TFLOP/s ({ms1:.3f} / {ms2:.3f} ms)")
+    assert 0 < tf1 <= 2600 and 0 < tf2 <= 2600
+    assert 1.6 < ms2 / ms1 < 2.4
+    assert float(sink[0]) == 0.0

@@ -6,7 +6,8 @@ every launch per kernel):
   or (steps run concurrently) one merge of all step partials follows (a CP path that silently drops ring steps runs fast with
   wrong gradients - "Hybrid / Hierarchical Context Parallel Skill", Pitfalls);
 * the padding decision by value gives the same launch sequence for an
-  aliased, NULL or distinct-equal cu_seqlens_padded;
+  aliased, NULL or distinct-equal cu_seqlens_padded, and for an asserted
+  pad_hint that agrees with the values;
 * tail zeroing is launched only when the local tensors have rows past the
   valid end.
 """
@@ -20,9 +21,9 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _launches(bt, cp, r, tail=0, cup="copy"):
+def _launches(bt, cp, r, tail=0, cup="copy", pad_hint=-1):
     db = H.DeviceBatch(bt)
-    meta, loc = H.local_inputs(db, cp, r, tail=tail, cup=cup)
+    meta, loc = H.local_inputs(db, cp, r, tail=tail, cup=cup, pad_hint=pad_hint)
     scale = 1.0 / math.sqrt(bt.d)
     import torch
     torch.cuda.synchronize()
@@ -60,6 +61,14 @@ def test_same_launches_for_alias_null_copy():
     bt, w = synth.make_workload(2)
     seqs = [_launches(bt, w["cp"], 1, cup=c) for c in ("copy", "alias", "null")]
     assert seqs[0] == seqs[1] == seqs[2]
+
+
+@pytest.mark.parametrize("cfg,hint", [(2, 0), (3, 1)])
+def test_same_launches_for_pad_hint(cfg, hint):
+    # an asserted hint that agrees with the values takes the path the
+    # value-based decision (-1) takes
+    bt, w = synth.make_workload(cfg)
+    assert _launches(bt, w["cp"], 1, pad_hint=hint) == _launches(bt, w["cp"], 1, pad_hint=-1)
 
 
 def test_tail_zero_gated():
