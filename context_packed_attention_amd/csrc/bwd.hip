@@ -19,6 +19,9 @@
 #ifndef DKDV_DESC
 #define DKDV_DESC 1
 #endif
+#ifndef DKDV_SPLIT_COPY
+#define DKDV_SPLIT_COPY 1
+#endif
 
 namespace cpattn {
 
@@ -249,7 +252,10 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
   constexpr int KB = DKDV_KB;
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
-  using QCopy = TileCopy<D, false, BQ, NWAVES, true>;  // Q and dO read both ways: permuted rows
+  // Q and dO are read both ways: permuted rows. With DKDV_SPLIT_COPY the
+  // first half of the wavefronts copies the Q tile and the second half the
+  // dO tile (whole chunk counts per wavefront, no per-chunk guards)
+  using QCopy = TileCopy<D, false, BQ, DKDV_SPLIT_COPY ? NWAVES / 2 : NWAVES, true>;
   using VCopy = TileCopy<D, false, BK, NWAVES>;
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][QCopy::BYTES / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][QCopy::BYTES / 2];
@@ -306,7 +312,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     const int ldb = (int)(p.ld_q * 2);
     const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 4;
     QCopy qc;  // the same plan serves Q and dO
-    qc.init(ldb, w, lane);
+    const int cw = DKDV_SPLIT_COPY ? w % (NWAVES / 2) : w;  // the wavefront's index among the tile's copiers
+    qc.init(ldb, cw, lane);
     // the step's first query row, and the head-to-head strides in bytes
     const char* q_base = reinterpret_cast<const char*>(p.q + (long long)qs * p.ld_q);
     const char* do_base = reinterpret_cast<const char*>(p.dout + (long long)qs * p.ld_q);
@@ -318,7 +325,15 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     // BIG: local query tensors of 2 GiB or more need 64-bit offsets; below
     // that the cheaper 32-bit scalar arithmetic serves
     auto issue = [&](int hh, int qt, int buf) {
-      if constexpr (BIG) {
+      if constexpr (DKDV_SPLIT_COPY) {
+        const bool first = w < NWAVES / 2;  // uniform: Q tile, else dO tile
+        const char* base = (first ? q_base : do_base) + hh * (D * 2);
+        uint16_t* dst = first ? Qs[buf] : Ds[buf];
+        if constexpr (BIG)
+          qc.copy(rsrc_from(base, (long long)qt * (BQ * ldb), q_end), dst, cw);
+        else
+          qc.copy(rsrc_from32(base, qt * (BQ * ldb), (int)q_end), dst, cw);
+      } else if constexpr (BIG) {
         const long long off = (long long)qt * (BQ * ldb);
         qc.copy(rsrc_from(q_base + hh * (D * 2), off, q_end), Qs[buf], w);
         qc.copy(rsrc_from(do_base + hh * (D * 2), off, q_end), Ds[buf], w);
