@@ -16,9 +16,6 @@
 #include "internal.h"
 #include "kern_common.h"
 
-#ifndef DKDV_DESC
-#define DKDV_DESC 1
-#endif
 #ifndef DKDV_SPLIT_COPY
 #define DKDV_SPLIT_COPY 1
 #endif
@@ -354,29 +351,23 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     };
     static_assert(sizeof(LD[0]) == BQ * 8, "lse / -D tile layout");
 
-#if DKDV_DESC
-    // query tiles last to first: every key block of a head starts on the same
-    // tile and the blocks move through the query rows together (shared L2)
-    int hh = kvh * p.group, qt = qt_end - 1;
-#else
-    int hh = kvh * p.group, qt = qt_begin;
-#endif
+    // query tiles last to first, and for each tile the group's query heads in
+    // turn: every key block of a KV head starts on the same tile and the
+    // blocks move down the query rows together, also at the causal step,
+    // where their sweeps end at different tiles (shared Q / dO tiles in L2)
+    const int h_first = kvh * p.group, h_last = h_first + p.group - 1;
+    int hh = h_first, qt = qt_end - 1;
     issue(hh, qt, 0);
     const int wkey_hi = k0 + wr0 + 32 * KB - 1;
     for (int it = 0; it < n_iter; ++it) {
       const int buf = it & 1;
       const int cur_qt = qt;
-#if DKDV_DESC
-      if (--qt < qt_begin) {
-        qt = qt_end - 1;
+      if (hh == h_last) {
+        hh = h_first;
+        --qt;
+      } else {
         ++hh;
       }
-#else
-      if (++qt == qt_end) {
-        qt = qt_begin;
-        ++hh;
-      }
-#endif
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (it + 1 < n_iter) issue(hh, qt, buf ^ 1);
