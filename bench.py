@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--all-gather", action="store_true",
                     help="time the all-gather share of the selected workload instead (gathered K/V in, the rank's "
                          "contribution to every gathered dK/dV row out) and exit")
+    ap.add_argument("--tail", type=int, default=0, metavar="ROWS",
+                    help="allocate the rank-local tensors ROWS rows past the valid end (the gradients' tail "
+                         "is then zeroed by one extra launch, whose HBM rate the kernel entry reports)")
     ap.add_argument("--pad-hint-abba", action="store_true",
                     help="only run the padding-decision A/B on the 16K pack (cu_seqlens_padded a distinct, "
                          "value-equal copy): steps with pad_hint -1 and 0 alternate in A B B A blocks of --steps "
@@ -415,7 +418,7 @@ def main():
     cu = torch.tensor(batch.cu, dtype=torch.int32, device="cuda")
     cup = torch.tensor(batch.cup, dtype=torch.int32, device="cuda")   # distinct, value-equal when unpadded
     T_local = int(batch.cup[-1]) // cp
-    t_alloc = T_local
+    t_alloc = T_local + max(0, args.tail)
     meta = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc)
     gq, gk, gv, gdo = (dev_bf16(x) for x in (batch.q, batch.k, batch.v, batch.do))
 
@@ -482,6 +485,12 @@ def main():
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
+    # algorithmic HBM bytes per launch of the HBM-bound kernels: bwd_pre reads
+    # dO and out (bf16) and the LSE and writes two fp32 planes; dq_finalize reads
+    # the fp32 accumulator and writes bf16 dQ; tail_zero writes the tail rows of
+    # dQ and of every dK / dV part
+    hbm_bytes = {"bwd_pre": T_local * hq * (4 * d + 12), "dq_finalize": T_local * hq * 6 * d,
+                 "tail_zero": 2 * (t_alloc - T_local) * (hq + 2 * cp * hkv) * d}
     kernels = {}
     for name, (ms, n) in per_kernel.items():
         entry = {"launches_per_step": n / args.steps, "ms_per_step": ms / args.steps, "avg_launch_ms": ms / n}
@@ -489,6 +498,9 @@ def main():
             fl = ALGO_FLOPS_PER_PAIR[name] * d * hq * pairs * args.steps
             entry["algo_tflops"] = fl / (ms * 1e-3) / 1e12
             entry["exec_tflops"] = EXEC_FLOPS_PER_PAIR[name] * d * hq * pairs * args.steps / (ms * 1e-3) / 1e12
+        if name in hbm_bytes:
+            entry["algo_bytes_per_launch"] = hbm_bytes[name]
+            entry["algo_GBps"] = hbm_bytes[name] * n / (ms * 1e-3) / 1e9
         kernels[name] = entry
     dom = max(per_kernel.items(), key=lambda kv: kv[1][0])[0]
     dom_ms, dom_n = per_kernel[dom]
@@ -565,7 +577,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO)",
         "config": {"workload": w["name"], "cp_size": cp, "cp_rank": rank, "tokens": batch.total_rows,
                    "t_local": T_local, "hq": hq, "hkv": hkv, "head_dim": d, "causal": True,
-                   "pairs": pairs, "step_pairs": step_pairs, "flops_per_step": flops_step,
+                   "pairs": pairs, "step_pairs": step_pairs, "flops_per_step": flops_step, "t_alloc": t_alloc,
                    "parallelism": "one CP rank's share, all ring steps on one GPU"},
         "metadata_call_ms": round(sorted(meta_ms)[len(meta_ms) // 2], 4),
         "kernels": kernels,
