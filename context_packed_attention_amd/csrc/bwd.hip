@@ -16,10 +16,6 @@
 #include "internal.h"
 #include "kern_common.h"
 
-#ifndef DKDV_SPLIT_COPY
-#define DKDV_SPLIT_COPY 1
-#endif
-
 namespace cpattn {
 
 struct BwdParams {
@@ -249,10 +245,11 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
   constexpr int KB = DKDV_KB;
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
-  // Q and dO are read both ways: permuted rows. With DKDV_SPLIT_COPY the
-  // first half of the wavefronts copies the Q tile and the second half the
-  // dO tile (whole chunk counts per wavefront, no per-chunk guards)
-  using QCopy = TileCopy<D, false, BQ, DKDV_SPLIT_COPY ? NWAVES / 2 : NWAVES, true>;
+  // Q and dO are read both ways: permuted rows. The first half of the
+  // wavefronts copies the Q tile and the second half the dO tile (whole
+  // chunk counts per wavefront, no per-chunk guards)
+  static_assert(NWAVES % 2 == 0, "the Q and dO tiles are copied by half the wavefronts each");
+  using QCopy = TileCopy<D, false, BQ, NWAVES / 2, true>;
   using VCopy = TileCopy<D, false, BK, NWAVES>;
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][QCopy::BYTES / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t Ds[2][QCopy::BYTES / 2];
@@ -309,7 +306,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     const int ldb = (int)(p.ld_q * 2);
     const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 4;
     QCopy qc;  // the same plan serves Q and dO
-    const int cw = DKDV_SPLIT_COPY ? w % (NWAVES / 2) : w;  // the wavefront's index among the tile's copiers
+    const int cw = w % (NWAVES / 2);  // the wavefront's index among the tile's copiers
     qc.init(ldb, cw, lane);
     // the step's first query row, and the head-to-head strides in bytes
     const char* q_base = reinterpret_cast<const char*>(p.q + (long long)qs * p.ld_q);
@@ -322,23 +319,13 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     // BIG: local query tensors of 2 GiB or more need 64-bit offsets; below
     // that the cheaper 32-bit scalar arithmetic serves
     auto issue = [&](int hh, int qt, int buf) {
-      if constexpr (DKDV_SPLIT_COPY) {
-        const bool first = w < NWAVES / 2;  // uniform: Q tile, else dO tile
-        const char* base = (first ? q_base : do_base) + hh * (D * 2);
-        uint16_t* dst = first ? Qs[buf] : Ds[buf];
-        if constexpr (BIG)
-          qc.copy(rsrc_from(base, (long long)qt * (BQ * ldb), q_end), dst, cw);
-        else
-          qc.copy(rsrc_from32(base, qt * (BQ * ldb), (int)q_end), dst, cw);
-      } else if constexpr (BIG) {
-        const long long off = (long long)qt * (BQ * ldb);
-        qc.copy(rsrc_from(q_base + hh * (D * 2), off, q_end), Qs[buf], w);
-        qc.copy(rsrc_from(do_base + hh * (D * 2), off, q_end), Ds[buf], w);
-      } else {
-        const int off = qt * (BQ * ldb);
-        qc.copy(rsrc_from32(q_base + hh * (D * 2), off, (int)q_end), Qs[buf], w);
-        qc.copy(rsrc_from32(do_base + hh * (D * 2), off, (int)q_end), Ds[buf], w);
-      }
+      const bool first = w < NWAVES / 2;  // uniform: Q tile, else dO tile
+      const char* base = (first ? q_base : do_base) + hh * (D * 2);
+      uint16_t* dst = first ? Qs[buf] : Ds[buf];
+      if constexpr (BIG)
+        qc.copy(rsrc_from(base, (long long)qt * (BQ * ldb), q_end), dst, cw);
+      else
+        qc.copy(rsrc_from32(base, qt * (BQ * ldb), (int)q_end), dst, cw);
       if (w == 0) {
         const int toff = qt * (BQ * 4);
         const __amdgpu_buffer_rsrc_t lr = rsrc_from32(l_base + hh * ld_head, toff, (int)ld_end);
