@@ -613,6 +613,138 @@ def share_keys_dkdv(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, s
     return dk, dv
 
 
+def group_row_stats(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float, kv_head: int,
+                    max_elems: int = 1 << 24) -> dict:
+    """First pass of the exact dK / dV of chosen key rows at any size: for
+    every valid query row p that rank r owns and every query head h of KV
+    group ``kv_head``, the row's softmax statistics
+
+        lse_{p,h} = log sum_{j <= p} exp(s_pj),   s_pj = scale <Q_p,h, K_j>
+        D_{p,h}   = <dO_p,h, out_p,h>,            out_p,h = sum_j P_pj V_j
+
+    with the exact float64 out, and (for the comparison tolerance, not the
+    method) var_D_{p,h} = sum_d (dO out)^2 + sum_j (P_pj dP_pj)^2, the sum the
+    rounding model of share_rounding_sd needs.
+
+    Each softmax row is whole (keys 0..p of its sequence); the rows are only
+    processed in batches of at most ``max_elems`` scores. Returns a dict with
+    "rows" (global query rows, int64 [n]), "seq", "pos" (sequence and
+    in-sequence position of each), and [group, n] float64 arrays "lse",
+    "dcoef", "var_d_terms".
+    """
+    cu, cup = validate(cu, cup, cp, r)
+    hq = q_bits.shape[1]
+    hkv = k_bits.shape[1]
+    if hq % hkv:
+        raise OracleError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    rank_of, _ = owner_map(cu, cup, cp)
+    rows, seq, pos = [], [], []
+    for b in range(cu.size - 1):
+        base = int(cup[b])
+        Lb = int(cu[b + 1] - cu[b])
+        p = np.nonzero(rank_of[base:base + Lb] == r)[0]
+        rows.append(base + p)
+        seq.append(np.full(p.size, b))
+        pos.append(p)
+    rows = np.concatenate(rows) if rows else np.zeros(0, np.int64)
+    seq = np.concatenate(seq) if seq else np.zeros(0, np.int64)
+    pos = np.concatenate(pos) if pos else np.zeros(0, np.int64)
+    n = rows.size
+    lse = np.full((group, n), NEG_INF)
+    dcoef = np.zeros((group, n))
+    var_terms = np.zeros((group, n))
+    kf = bf16_to_f64(k_bits[:, kv_head])
+    vf = bf16_to_f64(v_bits[:, kv_head])
+    for jh, h in enumerate(range(kv_head * group, (kv_head + 1) * group)):
+        i = 0
+        while i < n:
+            # a batch of rows of one sequence whose score block stays small
+            b = seq[i]
+            base = int(cup[b])
+            j = i
+            while j < n and seq[j] == b and (j - i + 1) * (int(pos[j]) + 1) <= max_elems:
+                j += 1
+            j = max(j, i + 1)
+            p = pos[i:j]
+            nk = int(p.max()) + 1
+            K, V = kf[base:base + nk], vf[base:base + nk]
+            Q = bf16_to_f64(q_bits[base + p, h])
+            dO = bf16_to_f64(do_bits[base + p, h])
+            s = scale * (Q @ K.T)
+            s = np.where(np.arange(nk)[None, :] <= p[:, None], s, NEG_INF)
+            m = s.max(axis=1)
+            l = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+            P = np.exp(s - l[:, None])
+            out = P @ V
+            dP = dO @ V.T
+            lse[jh, i:j] = l
+            dcoef[jh, i:j] = (dO * out).sum(axis=1)
+            var_terms[jh, i:j] = ((dO * out) ** 2).sum(axis=1) + ((P * dP) ** 2).sum(axis=1)
+            i = j
+    return {"rows": rows, "seq": seq, "pos": pos, "kv_head": kv_head, "group": group,
+            "lse": lse, "dcoef": dcoef, "var_d_terms": var_terms}
+
+
+def keys_dkdv_from_stats(stats: dict, q_bits, k_bits, v_bits, do_bits, cu, cup, scale: float, key_rows):
+    """Second pass: exact dK / dV of the given global key rows (of the stats'
+    KV head), from the first pass's per-row lse and D. For key j at position
+    k of sequence b:
+
+        dV_j = sum_{p, h} P_pj dO_p,h,   dK_j = scale sum_{p, h} dS_pj Q_p,h
+        P_pj = exp(s_pj - lse_p,h),      dS_pj = P_pj (<dO_p,h, V_j> - D_p,h)
+
+    over the stats' query rows p of sequence b at positions >= k and the
+    group's query heads h. Padding key rows get 0. Also returns the rounding
+    model's standard deviation of each element (as share_rounding_sd).
+    Returns dk, dv, dk_sd, dv_sd: [n_keys, D].
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    cup = np.asarray(cup, dtype=np.int64)
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    g, group = stats["kv_head"], stats["group"]
+    d = q_bits.shape[2]
+    c = BF16_UNIT_ROUNDOFF ** 2 / 3.0
+    dk = np.zeros((key_rows.size, d))
+    dv = np.zeros((key_rows.size, d))
+    var_dk = np.zeros((key_rows.size, d))
+    var_dv = np.zeros((key_rows.size, d))
+    for i, gk in enumerate(key_rows):
+        posk = _row_position(cu, cup, int(gk))
+        if posk is None:
+            continue
+        b, pk = posk
+        sel = np.nonzero((stats["seq"] == b) & (stats["pos"] >= pk))[0]
+        if sel.size == 0:
+            continue
+        kj = bf16_to_f64(k_bits[gk, g])
+        vj = bf16_to_f64(v_bits[gk, g])
+        for jh, h in enumerate(range(g * group, (g + 1) * group)):
+            Q = bf16_to_f64(q_bits[stats["rows"][sel], h])
+            dO = bf16_to_f64(do_bits[stats["rows"][sel], h])
+            P = np.exp(scale * (Q @ kj) - stats["lse"][jh, sel])
+            dS = P * (dO @ vj - stats["dcoef"][jh, sel])
+            dk[i] += scale * (dS @ Q)
+            dv[i] += P @ dO
+            var_D = c * stats["var_d_terms"][jh, sel]
+            var_dk[i] += c * scale ** 2 * ((dS ** 2) @ (Q ** 2)) + scale ** 2 * ((P ** 2) * var_D) @ (Q ** 2)
+            var_dv[i] += c * ((P ** 2) @ (dO ** 2))
+    return dk, dv, np.sqrt(var_dk), np.sqrt(var_dv)
+
+
+def share_keys_dkdv_two_pass(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
+                             shard: int, key_local_rows, kv_head: int, stats: dict | None = None):
+    """dK / dV rows of shard `shard`'s part of rank r's share for the selected
+    local key rows of one KV head, by the two passes above (the same values
+    as share_keys_dkdv, at a cost that does not grow with how many queries
+    reach a key). ``stats`` may hold a first pass already computed for this
+    rank and KV head. Returns dk, dv, dk_sd, dv_sd: [n_keys, D]."""
+    if stats is None:
+        stats = group_row_stats(q_bits, k_bits, v_bits, do_bits, cu, cup, cp, r, scale, kv_head)
+    krows = shard_rows(cu, cup, cp, shard)[np.asarray(key_local_rows, dtype=np.int64)]
+    return keys_dkdv_from_stats(stats, q_bits, k_bits, v_bits, do_bits, cu, cup, scale, krows)
+
+
 def flops_share(cu, cup, cp: int, r: int, hq: int, d: int) -> dict:
     """Algorithmic work of rank r's share: causal (query, key) pairs over valid
     rows (diagonal included) and the flop counts 4*D per pair per query head

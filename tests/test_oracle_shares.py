@@ -182,3 +182,48 @@ def test_dropped_ring_steps_would_fail_parity():
         own = O.attention(sub(bt.q), sub(bt.k), sub(bt.v), sub(bt.do), cu_loc, md["cu_padded_local"], scale)
         assert np.abs(own[0] - full["out"]).max() > 0.2
         assert np.abs(own[2] - full["dq"]).max() > 0.2
+
+
+@pytest.mark.parametrize("cp,hq,hkv,pad,seed", [(1, 4, 1, False, 31), (2, 4, 2, True, 32), (3, 6, 2, True, 33),
+                                                 (4, 8, 2, False, 34)])
+def test_two_pass_key_rows_match_full_share(cp, hq, hkv, pad, seed):
+    """The two-pass dK / dV (first pass: every rank row's lse and D; second:
+    chosen key rows) reproduces every row of every shard's part of the full
+    share, and its standard deviation the rounding model's, on packs with
+    GQA, padding and several ranks."""
+    bt = _random_batch(seed, cp, 3, hq, hkv, 8, pad)
+    scale = 0.31
+    T_local = bt.total_rows // cp
+    for r in range(cp):
+        sh = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
+        sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
+        for g in range(hkv):
+            # a small batch limit forces the first pass to split its rows
+            stats = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g, max_elems=40)
+            for s in range(cp):
+                keys = np.arange(T_local)
+                dk, dv, dks, dvs = O.share_keys_dkdv_two_pass(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r,
+                                                              scale, s, keys, g, stats=stats)
+                np.testing.assert_allclose(dk, sh["dk_parts"][s][:, g], rtol=1e-11, atol=1e-12)
+                np.testing.assert_allclose(dv, sh["dv_parts"][s][:, g], rtol=1e-11, atol=1e-12)
+                np.testing.assert_allclose(dks, sd["dk_parts"][s][:, g], rtol=1e-9, atol=1e-15)
+                np.testing.assert_allclose(dvs, sd["dv_parts"][s][:, g], rtol=1e-9, atol=1e-15)
+
+
+def test_two_pass_stats_are_the_rows_softmax():
+    """First-pass lse equals the share's LSE on every rank row, and D the
+    inner product of dO with the share's output."""
+    bt = _random_batch(41, 2, 3, 4, 2, 8, True)
+    scale = 0.4
+    sh = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, 2, 1, scale)
+    own = O.shard_rows(bt.cu, bt.cup, 2, 1)
+    loc = {int(g): i for i, g in enumerate(own)}
+    for g in range(2):
+        st = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, 2, 1, scale, g)
+        idx = np.array([loc[int(x)] for x in st["rows"]])
+        valid = O.valid_mask(bt.cu, bt.cup)[own]
+        assert valid[idx].all() and idx.size == int(valid.sum())
+        for jh, h in enumerate(range(2 * g, 2 * g + 2)):
+            np.testing.assert_allclose(st["lse"][jh], sh["lse"][h, idx], rtol=1e-12, atol=1e-12)
+            dref = (O.bf16_to_f64(bt.do[st["rows"], h]) * sh["out"][idx, h]).sum(axis=1)
+            np.testing.assert_allclose(st["dcoef"][jh], dref, rtol=1e-10, atol=1e-12)
