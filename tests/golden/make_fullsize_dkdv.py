@@ -1,0 +1,85 @@
+"""Write fullsize_dkdv.npz: exact dK / dV of sampled key rows of every source
+shard's part, at the two full-size shares the benchmark runs (the 131072-token
+GQA share, CP = 4, rank 2, and the 64K hierarchical pack's p2p share, CP = 2,
+rank 0), for one KV head each.
+
+Calls only the oracle (its two-pass key-row helper) and the seeded input
+generator; nothing comes from the HIP path. The inputs the values depend on
+(that KV head's K / V and its group's Q / dO, and the sequence tables) are
+hashed into the file, so a test reading it can tell that it still matches
+the generator. Run from the repository root:
+
+    python tests/golden/make_fullsize_dkdv.py
+"""
+import hashlib
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+from context_packed_attention_amd import synth  # noqa: E402
+from oracle import cp_attn_oracle as O  # noqa: E402
+
+OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fullsize_dkdv.npz")
+
+
+def key_rows(t_local: int, cu, cup, cp: int, shard: int) -> np.ndarray:
+    """Start, middle and end of the part, both chunk halves of the first and
+    last sequence slots, and a few seeded rows."""
+    half = t_local // 2
+    fixed = [0, 1, 31, 32, 127, half // 2, half - 1, half, half + 1, half + half // 2, t_local - 2, t_local - 1]
+    slot = np.asarray(cup) // cp
+    chunk = np.diff(np.asarray(cup)) // (2 * cp)
+    for b in (0, len(chunk) - 1):
+        fixed += [int(slot[b]), int(slot[b] + chunk[b]), int(slot[b] + chunk[b] - 1)]
+    rng = np.random.default_rng(1000 + shard)
+    fixed += list(rng.integers(0, t_local, 4))
+    return np.unique(np.clip(np.array(fixed, dtype=np.int64), 0, t_local - 1))
+
+
+def input_digest(bt, kv_head: int) -> str:
+    group = bt.hq // bt.hkv
+    hs = slice(kv_head * group, (kv_head + 1) * group)
+    h = hashlib.sha256()
+    for a in (np.asarray(bt.cu, np.int64), np.asarray(bt.cup, np.int64), bt.q[:, hs], bt.do[:, hs],
+              bt.k[:, kv_head], bt.v[:, kv_head]):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def main():
+    arrays = {}
+    for cfg in (4, 5):
+        bt, w = synth.make_workload(cfg)
+        cp, r = w["cp"], w["ranks"][-1]
+        g = bt.hkv - 1
+        scale = 1.0 / math.sqrt(bt.d)
+        t0 = time.time()
+        stats = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g)
+        print(f"{bt.name}: first pass over {stats['rows'].size} rows x {stats['group']} heads "
+              f"in {time.time() - t0:.1f} s", flush=True)
+        t_local = bt.total_rows // cp
+        pre = f"w{cfg}_"
+        arrays[pre + "meta"] = np.array([cp, r, g], dtype=np.int64)
+        arrays[pre + "digest"] = np.array(input_digest(bt, g))
+        for s in range(cp):
+            rows = key_rows(t_local, bt.cu, bt.cup, cp, s)
+            dk, dv, dks, dvs = O.share_keys_dkdv_two_pass(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale,
+                                                          s, rows, g, stats=stats)
+            arrays[pre + f"s{s}_rows"] = rows
+            # float32 keeps ~7 significant digits, far below any comparison bar
+            for name, a in (("dk", dk), ("dv", dv), ("dk_sd", dks), ("dv_sd", dvs)):
+                arrays[pre + f"s{s}_{name}"] = a.astype(np.float32)
+            print(f"  shard {s}: {rows.size} key rows, max |dk| {np.abs(dk).max():.4f}, "
+                  f"max |dv| {np.abs(dv).max():.4f}", flush=True)
+    np.savez_compressed(OUT, **arrays)
+    print("wrote", OUT, os.path.getsize(OUT), "bytes")
+
+
+if __name__ == "__main__":
+    main()

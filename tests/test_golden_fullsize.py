@@ -1,0 +1,41 @@
+"""The full-size dK / dV fixture (tests/golden/fullsize_dkdv.npz) still
+matches the seeded input generator (digest of the inputs its values depend
+on), and its values agree with the oracle's one-pass key-row routine on the
+key rows that routine computes cheaply (those few of the rank's queries
+reach), an independent path to the same numbers."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from context_packed_attention_amd import synth
+from oracle import cp_attn_oracle as O
+from tests.golden.make_fullsize_dkdv import OUT, input_digest
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_fixture_matches_generator_and_one_pass_oracle(cfg):
+    assert os.path.exists(OUT)
+    fx = np.load(OUT, allow_pickle=False)
+    bt, w = synth.make_workload(cfg)
+    pre = f"w{cfg}_"
+    cp, r, g = (int(x) for x in fx[pre + "meta"])
+    assert (cp, r) == (w["cp"], w["ranks"][-1]) and 0 <= g < bt.hkv
+    assert str(fx[pre + "digest"]) == input_digest(bt, g)
+    scale = 1.0 / math.sqrt(bt.d)
+    t_local = bt.total_rows // cp
+    rows = fx[pre + f"s{r}_rows"]
+    late = rows[rows >= t_local - 2]
+    assert late.size == 2
+    sel = np.searchsorted(rows, late)
+    dk, dv = O.share_keys_dkdv(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, r, late, [g])
+    np.testing.assert_allclose(fx[pre + f"s{r}_dk"][sel], dk[:, 0], rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(fx[pre + f"s{r}_dv"][sel], dv[:, 0], rtol=1e-5, atol=1e-7)
+    # every part has start, middle and end rows, and finite values
+    for s in range(cp):
+        rs = fx[pre + f"s{s}_rows"]
+        assert rs[0] == 0 and rs[-1] == t_local - 1 and (t_local // 2) in rs
+        for name in ("dk", "dv", "dk_sd", "dv_sd"):
+            a = fx[pre + f"s{s}_{name}"]
+            assert a.shape == (rs.size, bt.d) and np.isfinite(a).all()

@@ -2,10 +2,15 @@
 the 64K hierarchical-pack share), in the same launch configuration.
 
 The whole share is too large for the oracle, so: out / LSE / dQ are checked on
-sampled rows (each row one full softmax row of the oracle), dK / dV exactly on
-key rows that few of the rank's queries reach, every part's rows that no query
-of the rank reaches must be exactly zero, and four identities that hold at any
-size tie all rows of all parts together:
+sampled rows (each row one full softmax row of the oracle); dK / dV element by
+element on key rows at the start, middle and end of every source shard's part
+(so every ring step's launch, the causal one included, and key rows that all
+of the rank's queries reach), against values the oracle's two-pass helper
+computed once (tests/golden/make_fullsize_dkdv.py writes them, with a digest
+of the inputs they depend on); exactly on key rows that few of the rank's
+queries reach, computed here; every part's rows that no query of the rank
+reaches must be exactly zero; and four identities that hold at any size tie
+all rows of all parts together:
   sum_j dV_j = sum_p dO_p            (softmax rows sum to one)
   sum_j dK_j = 0                     (softmax is shift invariant)
   sum_p <dQ_p, Q_p> = sum_j <dK_j, K_j>   (both equal scale * sum dS_pj s_pj)
@@ -13,6 +18,7 @@ size tie all rows of all parts together:
 each per KV head, summed over the query heads of its group.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -89,6 +95,30 @@ def test_exact_key_rows_and_zero_rows(full):
         rows = O.shard_rows(bt.cu, bt.cup, cp, s)
         unreached = ~valid[rows] | (rows > last_q[seq[rows]])
         assert not res["dk"][s][unreached].any() and not res["dv"][s][unreached].any(), s
+
+
+FIXTURE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize_dkdv.npz")
+
+
+def test_dkdv_every_shard_vs_oracle_fixture(full):
+    """Key rows at the start, middle and end of every source shard's part
+    (both chunks), one KV head, element by element with the rounding model's
+    per-element standard deviation."""
+    from tests.golden.make_fullsize_dkdv import input_digest
+    bt, w, r, scale, res = full
+    cfg = 4 if bt.hkv != bt.hq else 5
+    fx = np.load(FIXTURE, allow_pickle=False)
+    pre = f"w{cfg}_"
+    cp, rank, g = (int(x) for x in fx[pre + "meta"])
+    assert (cp, rank) == (w["cp"], r)
+    assert str(fx[pre + "digest"]) == input_digest(bt, g), "fixture is stale: rerun tests/golden/make_fullsize_dkdv.py"
+    for s in range(cp):
+        rows = fx[pre + f"s{s}_rows"]
+        H.log(f"[full] shard {s}: {rows.size} key rows vs the fixture (kv head {g})")
+        a = H.compare_bf16(f"dk[{s}] rows", res["dk"][s][rows][:, g], fx[pre + f"s{s}_dk"], sd=fx[pre + f"s{s}_dk_sd"])
+        b = H.compare_bf16(f"dv[{s}] rows", res["dv"][s][rows][:, g], fx[pre + f"s{s}_dv"], sd=fx[pre + f"s{s}_dv_sd"])
+        H.log(f"    dk max {a['max_abs']:.2e} (max |ref| {a['max_ref']:.3f}), dv max {b['max_abs']:.2e} "
+              f"(max |ref| {b['max_ref']:.3f})")
 
 
 def _tol(vals):
