@@ -136,11 +136,69 @@ def run_bwd(meta, loc, bt, scale, out, lse, garbage: float = 5.0):
     return dq, dks, dvs
 
 
+# Every comparison's figures against the flat bar, for the session report
+# (tests/conftest.py writes them out): the count and maximum of elements over
+# max-abs 2e-2, also restricted to |ref| < 2 (where two bf16 ulps stay below
+# 2e-2), and the worst element with its error in units of the rounding
+# model's standard deviation.
+BAR_LOG: list = []
+
+
+def _flat_stats(err, ref, sd, got):
+    small = np.abs(ref) < 2.0
+    st = {"n": int(err.size), "n_over_2e-2": int((err > OUT_ATOL).sum()),
+          "max_abs": float(err.max()) if err.size else 0.0,
+          "n_over_2e-2_ref_lt_2": int((err[small] > OUT_ATOL).sum()),
+          "max_abs_ref_lt_2": float(err[small].max()) if small.any() else 0.0}
+    if err.size:
+        i = int(np.argmax(err))
+        idx = np.unravel_index(i, err.shape)
+        st["worst"] = {"index": [int(x) for x in idx], "got": float(got.flat[i]), "ref": float(ref.flat[i]),
+                       "sd": float(sd.flat[i]) if sd is not None else None,
+                       "z": float(err.flat[i] / sd.flat[i]) if sd is not None and sd.flat[i] > 0 else None}
+    return st
+
+
+def record_bar(name: str, st: dict, extra: dict | None = None):
+    import os
+    ent = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" (")[0], "tensor": name}
+    ent.update(st)
+    if extra:
+        ent.update(extra)
+    BAR_LOG.append(ent)
+    if st.get("n_over_2e-2", 0):
+        log(f"    [flat bar] {name}: {st['n_over_2e-2']} of {st['n']} elements over 2e-2 "
+            f"(max {st['max_abs']:.4f}; |ref| < 2: {st['n_over_2e-2_ref_lt_2']}, max {st['max_abs_ref_lt_2']:.4f}); "
+            f"worst {st.get('worst')}")
+
+
+def annotate_ideal(start: int, bt, cp: int, r: int, scale: float, refs: dict):
+    """For the comparisons recorded since BAR_LOG[start] that have elements
+    over max-abs 2e-2, compute the ideal forced-rounding implementation of
+    the same share (tests/ideal_rounding.py) and record its flat-bar figures
+    beside the GPU's. refs maps a recorded tensor name to (oracle array,
+    ideal key, part index or None)."""
+    ents = [e for e in BAR_LOG[start:] if e.get("n_over_2e-2") and e["tensor"] in refs]
+    if not ents:
+        return
+    from tests import ideal_rounding as IR
+    log(f"    [flat bar] computing the ideal forced-rounding share for {len(ents)} comparison(s)")
+    ideal = IR.ideal_share(bt, cp, r, scale)
+    for e in ents:
+        ref, key, part = refs[e["tensor"]]
+        arr = ideal[key] if part is None else ideal[key][part]
+        e["ideal"] = IR.flat_figures(arr, ref)
+        log(f"    [flat bar] {e['tensor']}: GPU {e['n_over_2e-2']} over / max {e['max_abs']:.4f}; "
+            f"ideal {e['ideal']['n_over_2e-2']} over / max {e['ideal']['max_abs']:.4f}")
+
+
 def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None, sd=None):
     """max-abs <= max(2e-2, two bf16 ulps of the reference, half an ulp + 6 sd)
     and relative L2 <= 1e-2; sd (optional) is the oracle's per-element
     standard deviation of the interface's forced roundings
-    (cp_attn_oracle.share_rounding_sd). Returns a stats dict."""
+    (cp_attn_oracle.share_rounding_sd). Every call also records how the
+    result fares against the flat max-abs 2e-2 (BAR_LOG). Returns a stats
+    dict."""
     got = bf16_bits_to_f64(got_bits)
     if rows is not None:
         got = got[rows]
@@ -165,9 +223,9 @@ def compare_bf16(name: str, got_bits: np.ndarray, ref: np.ndarray, rows=None, sd
     worst = float((err / tol).max()) if err.size else 0.0
     nref = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))
-    st = {"max_abs": float(err.max()) if err.size else 0.0, "worst_over_tol": worst, "rel_l2": rel,
-          "max_ref": float(np.abs(ref).max()) if ref.size else 0.0,
-          "n_over_2e-2": int((err > OUT_ATOL).sum())}
+    st = _flat_stats(err, ref, sd, got)
+    st.update({"worst_over_tol": worst, "rel_l2": rel, "max_ref": float(np.abs(ref).max()) if ref.size else 0.0})
+    record_bar(name, st)
     assert worst <= 1.0, f"{name}: max-abs {st['max_abs']:.3e} exceeds tolerance ({st})"
     assert rel <= OUT_REL_L2 or nref == 0.0, f"{name}: relative L2 {rel:.3e} > {OUT_REL_L2} ({st})"
     return st

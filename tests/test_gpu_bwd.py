@@ -33,6 +33,7 @@ def _check_bwd(bt, cp, ranks, tail=0):
         ref = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, want_grad=True)
         sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
         tl = loc["t_local"]
+        start = len(H.BAR_LOG)
         H.compare_bf16("out", H.bf16_to_np(out)[:tl], ref["out"], sd=sd["out"])
         dqb = H.bf16_to_np(dq)
         st = H.compare_bf16("dq", dqb[:tl], ref["dq"], sd=sd["dq"])
@@ -53,6 +54,11 @@ def _check_bwd(bt, cp, ranks, tail=0):
         if tail:
             assert not dqb[tl:].any(), "dq tail rows must be zeroed"
         H.log(f"    dq {st}")
+        refs = {"out": (ref["out"], "out", None), "dq": (ref["dq"], "dq", None)}
+        for s in range(cp):
+            refs[f"dk[{s}]"] = (ref["dk_parts"][s], "dk_parts", s)
+            refs[f"dv[{s}]"] = (ref["dv_parts"][s], "dv_parts", s)
+        H.annotate_ideal(start, bt, cp, r, scale, refs)
         meta.close()
 
 

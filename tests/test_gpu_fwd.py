@@ -33,7 +33,9 @@ def _check_fwd(bt, cp, ranks, tail=0, cup="copy"):
         sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
         tl = loc["t_local"]
         ob = H.bf16_to_np(out)
+        start = len(H.BAR_LOG)
         st = H.compare_bf16("out", ob[:tl], ref["out"], sd=sd["out"])
+        H.annotate_ideal(start, bt, cp, r, scale, {"out": (ref["out"], "out", None)})
         lt = lse.cpu().numpy()
         sl = H.compare_lse("lse", lt[:, :tl], ref["lse"])
         rows = O.shard_rows(bt.cu, bt.cup, cp, r)

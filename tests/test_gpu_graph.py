@@ -5,13 +5,18 @@ fixed reduction order). Replays are checked one by one with eager work and
 synchronisations between them, again after the inputs change in place, and
 the graph must hold exactly the eager launch sequence ("[PyTorch][Attention]
 THD P2P context-parallel regression ...", "Expected behavior": padding
-metadata that is safe under graph capture)."""
+metadata that is safe under graph capture). The first replay and the replay
+after the inputs change are also compared with the fp64 oracle (all heads of
+the tiny pack; two KV heads and their query-head groups of the larger packs,
+whose heads are independent problems)."""
+import copy
 import math
 
 import numpy as np
 import pytest
 
 from context_packed_attention_amd import api, synth
+from oracle import cp_attn_oracle as O
 from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
@@ -21,6 +26,34 @@ def _same(name, a, b):
     import torch
     assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"{name} differs from the eager result"
+
+
+def _sub_heads(bt, kv_heads):
+    """The batch restricted to some KV heads and their query-head groups."""
+    group = bt.hq // bt.hkv
+    qh = [g * group + j for g in kv_heads for j in range(group)]
+    sub = copy.copy(bt)
+    sub.q, sub.do = bt.q[:, qh], bt.do[:, qh]
+    sub.k, sub.v = bt.k[:, kv_heads], bt.v[:, kv_heads]
+    sub.hq, sub.hkv = len(qh), len(kv_heads)
+    return sub, qh
+
+
+def _vs_oracle(tag, bt, cp, rank, scale, tl, res):
+    out, lse, dq, dks, dvs = res
+    kv_heads = list(range(bt.hkv)) if bt.hkv * (bt.hq // bt.hkv) <= 4 else sorted({0, bt.hkv - 1})
+    sub, qh = _sub_heads(bt, kv_heads)
+    H.log(f"[graph] {tag}: oracle on kv heads {kv_heads}")
+    ref = O.share(sub.q, sub.k, sub.v, sub.do, sub.cu, sub.cup, cp, rank, scale)
+    sd = O.share_rounding_sd(sub.q, sub.k, sub.v, sub.do, sub.cu, sub.cup, cp, rank, scale)
+    H.compare_bf16(f"{tag} out", H.bf16_to_np(out)[:tl][:, qh], ref["out"], sd=sd["out"])
+    H.compare_lse(f"{tag} lse", lse.cpu().numpy()[qh][:, :tl], ref["lse"])
+    H.compare_bf16(f"{tag} dq", H.bf16_to_np(dq)[:tl][:, qh], ref["dq"], sd=sd["dq"])
+    for s in range(cp):
+        H.compare_bf16(f"{tag} dk[{s}]", H.bf16_to_np(dks[s])[:tl][:, kv_heads], ref["dk_parts"][s],
+                       sd=sd["dk_parts"][s])
+        H.compare_bf16(f"{tag} dv[{s}]", H.bf16_to_np(dvs[s])[:tl][:, kv_heads], ref["dv_parts"][s],
+                       sd=sd["dv_parts"][s])
 
 
 # the padded pack of test_gpu_inorder: long enough for the in-order launch plan
@@ -81,6 +114,8 @@ def test_graph_replays_match_eager(cfg, rank, tail):
         torch.cuda.synchronize()
         check(ref)
         H.log(f"[graph] replay {rep} matches")
+        if rep == 0:
+            _vs_oracle("replay 0", bt, cp, rank, scale, tl, (out, lse, dq, dks, dvs))
     # the graph reads its inputs' current contents
     loc["q"].mul_(0.5)
     loc["do"].mul_(-1.0)
@@ -89,6 +124,11 @@ def test_graph_replays_match_eager(cfg, rank, tail):
     torch.cuda.synchronize()
     check(ref2)
     assert not torch.equal(ref2[2].view(torch.int16), ref[2].view(torch.int16))
+    # the oracle on the changed inputs (halving and negating are exact in bf16)
+    bt2 = copy.copy(bt)
+    bt2.q = synth.f32_to_bf16_bits((O.bf16_to_f64(bt.q) * 0.5).astype(np.float32))
+    bt2.do = bt.do ^ np.uint16(0x8000)
+    _vs_oracle("changed inputs", bt2, cp, rank, scale, tl, (out, lse, dq, dks, dvs))
     g.close()
     meta.close()
 

@@ -24,11 +24,7 @@ import pytest
 
 from context_packed_attention_amd import synth
 from oracle import cp_attn_oracle as O
-
-
-def _round_bf16(x):
-    bits = synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
-    return O.bf16_to_f64(bits)
+from tests import ideal_rounding as IR
 
 
 def _ulp(x):
@@ -36,35 +32,10 @@ def _ulp(x):
 
 
 def _ideal_bf16_share(bt, scale):
-    """CP = 1 share (all rows, global order) computed with only the forced
-    roundings: out = bf16((bf16(P~) V) / l), D from that out, dS and P as
-    bf16 operands, every result rounded to bf16."""
-    q, k, v, do = (O.bf16_to_f64(x) for x in (bt.q, bt.k, bt.v, bt.do))
-    T, hq, d = q.shape
-    hkv = k.shape[1]
-    group = hq // hkv
-    res = {n: np.zeros(x.shape) for n, x in (("out", q), ("dq", q), ("dk", k), ("dv", k))}
-    for b in range(bt.cu.size - 1):
-        s0, n = int(bt.cup[b]), int(bt.cu[b + 1] - bt.cu[b])
-        if n == 0:
-            continue
-        for h in range(hq):
-            g = h // group
-            K, V, Q, dO = k[s0:s0 + n, g], v[s0:s0 + n, g], q[s0:s0 + n, h], do[s0:s0 + n, h]
-            S = scale * (Q @ K.T)
-            S[np.triu_indices(n, 1)] = -np.inf
-            Pt = np.exp(S - S.max(axis=1, keepdims=True))
-            lsum = Pt.sum(axis=1, keepdims=True)
-            out_b = _round_bf16((_round_bf16(Pt) @ V) / lsum)
-            P = Pt / lsum
-            dS_b = _round_bf16(P * (dO @ V.T - (dO * out_b).sum(axis=1, keepdims=True)))
-            res["out"][s0:s0 + n, h] = out_b
-            res["dq"][s0:s0 + n, h] = _round_bf16(scale * (dS_b @ K))
-            res["dk"][s0:s0 + n, g] += scale * (dS_b.T @ Q)
-            res["dv"][s0:s0 + n, g] += _round_bf16(P).T @ dO
-    res["dk"] = _round_bf16(res["dk"])
-    res["dv"] = _round_bf16(res["dv"])
-    return res
+    """CP = 1 share (all rows, global order) with only the forced roundings
+    (tests/ideal_rounding.py)."""
+    res = IR.ideal_share(bt, 1, 0, scale)
+    return {"out": res["out"], "dq": res["dq"], "dk": res["dk_parts"][0], "dv": res["dv_parts"][0]}
 
 
 def _packs():
