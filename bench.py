@@ -545,10 +545,12 @@ def main():
     gmeta.close()
 
     # attainable matrix-unit rate on this device: the library's calibration
-    # kernel (nothing but independent MFMA chains), best of three launches
+    # kernel (nothing but independent MFMA chains on toggling pseudo-random
+    # operands), sustained: 40 back-to-back launches (about 0.6 s, long
+    # enough for the power limit to set the clock), the median of the last 20
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    probes = [api.cp_attn_mfma_probe(100000, sink, stream=stream) for _ in range(3)]
-    attainable = max(tf for _, tf in probes)
+    probes = [api.cp_attn_mfma_probe(100000, sink, stream=stream) for _ in range(40)]
+    attainable = float(np.median([tf for _, tf in probes[20:]]))
     log(f"[bench] matrix-unit calibration: {attainable:.1f} TFLOP/s attainable")
     if roof.get("bound") == "mfma":
         roof["attainable_peak"] = round(attainable, 1)
@@ -584,8 +586,10 @@ def main():
         "roofline": roof,
         "graph": graph_info,
         "mfma_calibration": {"attainable_tflops": round(attainable, 1),
-                             "launch_ms": [round(m, 3) for m, _ in probes],
-                             "kernel": "independent v_mfma_f32_32x32x16_bf16 chains, 8 per SIMD, no memory traffic"},
+                             "launch_ms_first_last": [round(probes[0][0], 3), round(probes[-1][0], 3)],
+                             "kernel": "independent v_mfma_f32_32x32x16_bf16 chains on rotating pseudo-random "
+                                       "bf16 operands, 8 per SIMD, no memory traffic; median of launches 21-40 "
+                                       "of 40 back to back"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -63,22 +63,47 @@ void timing_end(hipStream_t st) {
 // Matrix-unit calibration: four independent v_mfma_f32_32x32x16_bf16 chains
 // per wavefront on register operands (no memory traffic in the loop), two
 // 4-wavefront blocks per compute unit, so every SIMD keeps eight chains in
-// flight. The sum is stored only if it hits an impossible value, which keeps
-// the chains live without writing anything.
-__global__ void __launch_bounds__(256, 2) mfma_probe_kernel(int iters, float* sink) {
-  const int lane = threadIdx.x & 63;
-  bf16x8_t a, b;
+// flight. The operands rotate through eight sets of pseudo-random bf16
+// values per lane: the matrix unit's power, and so the clock the chip holds
+// under a power limit, depends on how many operand bits toggle, and constant
+// operands would report a rate that real data never reaches. The sum is
+// stored only if it hits an impossible value, which keeps the chains live
+// without writing anything.
+__device__ __forceinline__ unsigned probe_hash(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__device__ __forceinline__ bf16x8_t probe_operand(unsigned seed) {
+  bf16x8_t v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)((float)((lane + e) & 7) * 1e-3f);
-    b[e] = (__bf16)((float)((lane * 3 + e) & 7) * 1e-3f);
+    const unsigned h = probe_hash(seed * 8u + (unsigned)e);
+    v[e] = (__bf16)((float)((int)(h & 0xffffu) - 32768) * (1.0f / 16384.f));  // uniform in [-2, 2)
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(256, 2) mfma_probe_kernel(int iters, float* sink) {
+  const unsigned seed = (blockIdx.x * 256u + threadIdx.x) * 16u;
+  bf16x8_t a[8], b[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    a[r] = probe_operand(seed + r);
+    b[r] = probe_operand(seed + 8 + r);
   }
   f32x16_t acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = zero16();
-  for (int i = 0; i < iters; ++i) {
+  for (int i = 0; i < iters; i += 8) {  // eight products per chain per pass
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = mfma32x32x16(a, b, acc[c]);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = mfma32x32x16(a[(u + c) & 7], b[(3 * u + c) & 7], acc[c]);
   }
   float s = 0.f;
 #pragma unroll
@@ -117,7 +142,8 @@ extern "C" cp_attn_status cp_attn_mfma_probe(int32_t iters, float* sink, void* s
   (void)hipEventDestroy(e1);
   if (rc != CP_ATTN_OK) return rc;
   *ms = t;
-  *tflops = (double)blocks * 4 * 4 * (double)iters * (32.0 * 32 * 16 * 2) / (t * 1e-3) / 1e12;
+  const double products = (double)((iters + 7) / 8 * 8);  // per chain
+  *tflops = (double)blocks * 4 * 4 * products * (32.0 * 32 * 16 * 2) / (t * 1e-3) / 1e12;
   return CP_ATTN_OK;
 }
 

@@ -338,11 +338,12 @@ int32_t cp_attn_timing_read(char* names, int32_t name_len, double* total_ms, int
 /*
  * Attainable bf16 matrix-unit rate (measurement tooling, not on the numerical
  * path): one launch of independent v_mfma_f32_32x32x16_bf16 chains on register
- * operands, two 256-thread blocks per compute unit of the current device,
- * `iters` products per chain, timed with HIP events on `stream` (the call
- * waits for it). Reports the launch's milliseconds and its dense bf16
- * TFLOP/s, the rate the attention kernels can reach at the clock the device
- * holds under matrix load. `sink`: device float, written only in a case that
+ * operands that rotate through pseudo-random bf16 values (so operand bits
+ * toggle as with real data), two 256-thread blocks per compute unit of the
+ * current device, `iters` products per chain (rounded up to a multiple of 8),
+ * timed with HIP events on `stream` (the call waits for it). Reports the
+ * launch's milliseconds and its dense bf16 TFLOP/s: the rate the matrix unit
+ * sustains on data at the clock the device holds under its power limit. `sink`: device float, written only in a case that
  * cannot occur (keeps the products live). Errors: CP_ATTN_ERR_INVALID_ARG for
  * iters <= 0 or a NULL pointer, CP_ATTN_ERR_HIP for a failed launch.
  */
