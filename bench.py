@@ -80,6 +80,12 @@ def parse():
     ap.add_argument("--a2a", action="store_true",
                     help="only time the hierarchical front end's all-to-all (sequence split -> head split and back) "
                          "on the 64K hierarchical pack, [a2a, p2p] = [2, 2], Q of 32 heads, and exit")
+    ap.add_argument("--hier", action="store_true",
+                    help="time one whole a2a+p2p step of an a2a group on the 64K hierarchical pack "
+                         "([a2a, p2p] = [2, 2], CP = 4, 32 heads before the head split): sequence -> head "
+                         "all-to-all of Q, K, V (and dO), the p2p-level share of each head group, forward and "
+                         "backward, and the head -> sequence all-to-all of out, dQ and the own shard's dK / dV; "
+                         "print one JSON line and exit")
     ap.add_argument("--all-gather", action="store_true",
                     help="time the all-gather share of the selected workload instead (gathered K/V in, the rank's "
                          "contribution to every gathered dK/dV row out) and exit")
@@ -90,10 +96,91 @@ def parse():
                     help="only run the padding-decision A/B on the 16K pack (cu_seqlens_padded a distinct, "
                          "value-equal copy): steps with pad_hint -1 and 0 alternate in A B B A blocks of --steps "
                          "steps, repeated three times; print both step times and launch sequences and exit")
+    ap.add_argument("--phases", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the power / clock phases on the selected workload and exit: the matrix-unit "
+                         "calibration, the forward alone and the backward alone, each back to back for SECONDS, "
+                         "with amd-smi sampled in the background (socket power, per-XCD graphics clocks)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and exit "
                          "(the known-size reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+class SmiSampler:
+    """Background sampling of the GPU's socket power and per-XCD graphics
+    clocks through the amd-smi command-line tool (one call at a time)."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self.stop = threading.Event()
+        self.th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import subprocess
+        while not self.stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                t = time.time()
+                o = json.loads(r.stdout)
+                g = o["gpu_data"][0] if isinstance(o, dict) else o[0]
+                clk = [g["clock"][f"gfx_{x}"]["clk"]["value"] for x in range(8) if f"gfx_{x}" in g["clock"]]
+                self.samples.append((t, float(g["power"]["socket_power"]["value"]), [float(c) for c in clk]))
+            except Exception:
+                time.sleep(0.2)
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *a):
+        self.stop.set()
+        self.th.join(timeout=15)
+
+    def between(self, t0, t1):
+        """Mean power and per-XCD clocks of the samples inside [t0, t1] (the
+        first 0.5 s left out: the tool reports with some lag)."""
+        sel = [x for x in self.samples if t0 + 0.5 <= x[0] <= t1]
+        if not sel:
+            return None
+        n = len(sel[0][2])
+        clk = [sum(x[2][i] for x in sel) / len(sel) for i in range(n)]
+        return {"samples": len(sel), "socket_power_w": round(sum(x[1] for x in sel) / len(sel), 1),
+                "gfx_mhz_mean": round(sum(clk) / n, 1), "gfx_mhz_per_xcd": [round(c) for c in clk]}
+
+
+def power_phases(seconds, fwd, bwd, probe, flops_fwd, flops_bwd):
+    """Each phase back to back for `seconds`: its rate and, from amd-smi, the
+    socket power and graphics clocks it ran at."""
+    import torch
+    out = {}
+    with SmiSampler() as smi:
+        time.sleep(1.0)
+        for name, fn, flops in (("mfma_calibration", probe, None), ("forward", fwd, flops_fwd),
+                                ("backward", bwd, flops_bwd)):
+            torch.cuda.synchronize()
+            t0 = time.time()
+            n, tf = 0, []
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            while time.time() - t0 < seconds:
+                r = fn()
+                if flops is None:
+                    tf.append(r)
+                n += 1
+                if n % 4 == 0:
+                    torch.cuda.synchronize()
+            e1.record()
+            torch.cuda.synchronize()
+            t1 = time.time()
+            ms = e0.elapsed_time(e1) / n
+            rate = (sorted(tf)[len(tf) // 2] if flops is None else flops / (ms * 1e-3) / 1e12)
+            out[name] = {"launches": n, "ms_each": round(ms, 3), "tflops": round(rate, 1), "smi": smi.between(t0, t1)}
+            log(f"[phases] {name}: {n} calls, {ms:.3f} ms each, {rate:.1f} TFLOP/s, {out[name]['smi']}")
+            time.sleep(1.0)
+    return out
 
 
 def copy_calibration(mib):
@@ -203,6 +290,123 @@ def a2a_bench(args):
         "roofline": {"kernel": "a2a_seq_to_head", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
     }
+    print(json.dumps(line), flush=True)
+
+
+def hier_bench(args):
+    """One a2a+p2p step of a2a group p = 0 on the 64K hierarchical pack, all
+    on one GPU: both a2a ranks' work (CP ranks 0 and 1, head groups 0 and 1).
+    The K / V of the p2p ring's other shard arrive over the ring in a real
+    run (the other group's all-to-all makes them), so they are inputs here,
+    head-split already; likewise that shard's dK / dV parts leave over the
+    ring. Timed: seq -> head of Q, K, V, the forward share of each head
+    group, head -> seq of out; seq -> head of dO, the backward share of each
+    head group, head -> seq of dQ, dK and dV of the own shard."""
+    import numpy as np
+    import torch
+    from context_packed_attention_amd import api, synth
+    w = synth.workload(5)
+    A, P = 2, 2
+    cp = A * P
+    L = w["lengths"]
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    H, d = 2 * w["hq"], w["d"]  # heads before the split (query and key / value alike)
+    hs = H // A
+    T = int(cu[-1])
+    tl_cp, tl_p = T // cp, T // P
+    scale = 1.0 / math.sqrt(d)
+    dcu = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    dcup = dcu.clone()
+    m_cp = api.cp_attn_rank_metadata(dcu, dcup, cp, 0, -1, tl_cp)
+    m_p = api.cp_attn_rank_metadata(dcu, dcup, P, 0, -1, tl_p)
+    pairs = sum(api.step_pairs(m_p))
+    flops_step = A * 14 * d * hs * pairs
+    nd = synth.device_normal_bf16
+    # CP-level rows of CP ranks 0 and 1, all heads
+    q_cp = [nd((tl_cp, H, d), 50 + a) for a in range(A)]
+    k_cp = [nd((tl_cp, H, d), 60 + a) for a in range(A)]
+    v_cp = [nd((tl_cp, H, d), 70 + a) for a in range(A)]
+    do_cp = [nd((tl_cp, H, d), 80 + a) for a in range(A)]
+    # the ring's other shard (p2p rank 1), per head group
+    k_s1 = [nd((tl_p, hs, d), 90 + a) for a in range(A)]
+    v_s1 = [nd((tl_p, hs, d), 95 + a) for a in range(A)]
+    e = lambda shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    q_h, k_h, v_h, do_h = ([e((tl_p, hs, d)) for _ in range(A)] for _ in range(4))
+    out_h, dq_h = [e((tl_p, hs, d)) for _ in range(A)], [e((tl_p, hs, d)) for _ in range(A)]
+    lse_h = [torch.empty((hs, tl_p), dtype=torch.float32, device="cuda") for _ in range(A)]
+    dk_h = [[e((tl_p, hs, d)) for _ in range(P)] for _ in range(A)]
+    dv_h = [[e((tl_p, hs, d)) for _ in range(P)] for _ in range(A)]
+    out_cp, dq_cp, dk_cp, dv_cp = ([e((tl_cp, H, d)) for _ in range(A)] for _ in range(4))
+    ws_f = torch.empty(api.cp_attn_workspace_bytes(m_p, hs, hs, d, 0), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(api.cp_attn_workspace_bytes(m_p, hs, hs, d, 1), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+    s2h = lambda ins, outs: api.cp_attn_a2a_seq_to_head(m_cp, A, 0, H, d * 2, ins, outs, stream=st)
+    h2s = lambda ins, outs: api.cp_attn_a2a_head_to_seq(m_cp, A, 0, H, d * 2, ins, outs, stream=st)
+
+    def step():
+        s2h(q_cp, q_h)
+        s2h(k_cp, k_h)
+        s2h(v_cp, v_h)
+        for a in range(A):
+            api.cp_attn_fwd(m_p, q_h[a], [k_h[a], k_s1[a]], [v_h[a], v_s1[a]], hs, hs, d, scale, 1, out_h[a],
+                            lse_h[a], ws_f, stream=st)
+        h2s(out_h, out_cp)
+        s2h(do_cp, do_h)
+        for a in range(A):
+            api.cp_attn_bwd(m_p, q_h[a], [k_h[a], k_s1[a]], [v_h[a], v_s1[a]], out_h[a], lse_h[a], do_h[a], hs, hs,
+                            d, scale, 1, dq_h[a], dk_h[a], dv_h[a], ws_b, stream=st)
+        h2s(dq_h, dq_cp)
+        h2s([dk_h[a][0] for a in range(A)], dk_cp)
+        h2s([dv_h[a][0] for a in range(A)], dv_cp)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    api.cp_attn_timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    api.cp_attn_timing_enable(False)
+    per_kernel = api.cp_attn_timing_read()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flops_step / (ms * 1e-3) / 1e12
+    perm_bytes = 2 * A * tl_cp * H * d * 2  # one all-to-all call reads and writes this
+    kernels = {}
+    for name, (kms, n) in per_kernel.items():
+        ent = {"launches_per_step": n / args.steps, "ms_per_step": kms / args.steps, "avg_launch_ms": kms / n}
+        if name in ALGO_FLOPS_PER_PAIR:
+            ent["algo_tflops"] = ALGO_FLOPS_PER_PAIR[name] * d * hs * pairs * A * args.steps / (kms * 1e-3) / 1e12
+        if name.startswith("a2a_"):
+            ent["algo_GBps"] = perm_bytes * n / (kms * 1e-3) / 1e9
+        kernels[name] = ent
+    dom = max(per_kernel.items(), key=lambda kv: kv[1][0])[0]
+    dms, dn = per_kernel[dom]
+    roof = {"kernel": dom, "bound": "mfma", "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS, "traffic": None}
+    if dom in ALGO_FLOPS_PER_PAIR:
+        per_launch = ALGO_FLOPS_PER_PAIR[dom] * d * hs * pairs * A * args.steps / dn
+        roof.update({"achieved": round(per_launch / (dms / dn * 1e-3) / 1e12, 2), "algo_flops_per_launch": per_launch,
+                     "avg_launch_ms": dms / dn})
+        roof["frac"] = round(roof["achieved"] / BF16_PEAK_TFLOPS, 4)
+    a2a_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("a2a_"))
+    log(f"[bench] hierarchical step {ms:.3f} ms, {tflops:.1f} TFLOP/s; all-to-all {a2a_ms:.3f} ms of it")
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s per CP-rank share (1 MI355X), % of bf16 MFMA peak",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, drawn on the device)",
+        "config": {"workload": w["name"] + "-a2a+p2p-step", "a2a_size": A, "p2p_size": P, "cp_size": cp,
+                   "heads_before_split": H, "heads_per_group": hs, "head_dim": d, "tokens": T,
+                   "p2p_t_local": tl_p, "pairs_per_group": pairs, "flops_per_step": flops_step,
+                   "parallelism": "one a2a group's step (both a2a ranks) on one GPU"},
+        "all_to_all_ms_per_step": round(a2a_ms, 4), "all_to_all_bytes_per_call": perm_bytes,
+        "kernels": kernels, "roofline": roof,
+    }
+    m_cp.close()
+    m_p.close()
     print(json.dumps(line), flush=True)
 
 
@@ -400,6 +604,9 @@ def main():
     if args.all_gather:
         ag_bench(args)
         return
+    if args.hier:
+        hier_bench(args)
+        return
     if args.pad_hint_abba:
         abba_bench(args)
         return
@@ -443,6 +650,18 @@ def main():
     pairs = sum(step_pairs)
     flops_step = 14 * d * hq * pairs
     stream = torch.cuda.current_stream()
+    if args.phases > 0:
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+        res = power_phases(
+            args.phases,
+            lambda: api.cp_attn_fwd(meta, q, ks, vs, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream),
+            lambda: api.cp_attn_bwd(meta, q, ks, vs, out, lse, do, hq, hkv, d, scale, 1, dq, dks, dvs, ws_b,
+                                    stream=stream),
+            lambda: api.cp_attn_mfma_probe(100000, sink, stream=stream)[1],
+            4 * d * hq * pairs, 10 * d * hq * pairs)
+        print(json.dumps({"workload": w["name"], "phases": res}), flush=True)
+        meta.close()
+        return
     meta.close()
 
     # host-side cost of one metadata build on an idle device (it ends in the

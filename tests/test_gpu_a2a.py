@@ -133,3 +133,84 @@ def test_hierarchical_share_end_to_end():
             H.log(f"    CP rank {c} dq {st['max_abs']:.2e} / {st['rel_l2']:.2e}")
         m_p.close()
     m_cp.close()
+
+
+def test_hierarchical_step_full_pack_sampled():
+    """The whole a2a+p2p step of a2a group 0 on the 64K hierarchical pack
+    (the benchmark's --hier workload: [2, 2], 32 heads before the split),
+    end to end through both all-to-alls; sampled rows of the CP-level out,
+    LSE and dQ of CP ranks 0 and 1, and the CP-level dK / dV of late key rows
+    of their own shards (the contribution of the group's queries), against
+    the oracle's CP = 4 shares."""
+    import torch
+    A, P = 2, 2
+    cp = A * P
+    w = synth.workload(5)
+    L = w["lengths"]
+    H_, d = 2 * w["hq"], w["d"]
+    hs = H_ // A
+    bt = synth.make_batch("pack64k-hier-32heads", 1005, L, L, H_, H_, d)
+    scale = 1.0 / math.sqrt(d)
+    db = H.DeviceBatch(bt)
+    T = int(bt.cup[-1])
+    tl_cp, tl_p = T // cp, T // P
+    m_cp = api.cp_attn_rank_metadata(db.cu, db.cup, cp, 0, -1, tl_cp)
+
+    def cp_shard(src, c):
+        dst = torch.zeros((tl_cp, H_, d), dtype=torch.bfloat16, device="cuda")
+        api.cp_attn_shard_gather(m_cp, c, src, dst, H_ * d * 2)
+        return dst
+
+    def split(src, p):
+        outs = [torch.empty((tl_p, hs, d), dtype=torch.bfloat16, device="cuda") for _ in range(A)]
+        api.cp_attn_a2a_seq_to_head(m_cp, A, p, H_, d * 2, [cp_shard(src, p * A + a) for a in range(A)], outs)
+        return outs
+
+    H.log("[hier-full] all-to-all of Q, K, V, dO")
+    q_h, do_h = split(db.q, 0), split(db.do, 0)
+    k_h = [split(db.k, p) for p in range(P)]
+    v_h = [split(db.v, p) for p in range(P)]
+    m_p = api.cp_attn_rank_metadata(db.cu, db.cup, P, 0, -1, tl_p)
+    outs, lses, dqs, dks, dvs = [], [], [], [], []
+    for a in range(A):
+        H.log(f"[hier-full] p2p share of head group {a}")
+        loc = {"q": q_h[a], "do": do_h[a], "k": [k_h[s][a] for s in range(P)], "v": [v_h[s][a] for s in range(P)],
+               "t_alloc": tl_p, "t_local": tl_p}
+        sub = synth.PackedBatch(name="sub", seed=0, cu=bt.cu, cup=bt.cup, hq=hs, hkv=hs, d=d, q=None, k=None,
+                                v=None, do=None)
+        out, lse = H.run_fwd(m_p, loc, sub, scale)
+        dq, dk, dv = H.run_bwd(m_p, loc, sub, scale, out, lse)
+        outs.append(out)
+        lses.append(lse)
+        dqs.append(dq)
+        dks.append(dk[0])
+        dvs.append(dv[0])
+    back = {}
+    for name, src in (("out", outs), ("dq", dqs), ("dk", dks), ("dv", dvs)):
+        back[name] = [torch.empty((tl_cp, H_, d), dtype=torch.bfloat16, device="cuda") for _ in range(A)]
+        api.cp_attn_a2a_head_to_seq(m_cp, A, 0, H_, d * 2, src, back[name])
+    torch.cuda.synchronize()
+    # LSE back to the sequence split by the oracle's own permutation of
+    # [rows, heads] arrays (the LSE planes are [heads, rows] on the device)
+    lse_cp = O.a2a_head_to_seq([l.cpu().numpy().T.copy() for l in lses], bt.cup, cp, A, 0)
+    rng = np.random.default_rng(5)
+    heads = [0, 7, 16, 31]
+    for a in range(A):
+        c = a  # CP rank of group 0, a2a rank a
+        rows = np.unique(np.concatenate([[0, 1, tl_cp // 2, tl_cp - 1], rng.integers(0, tl_cp, 12)]))
+        H.log(f"[hier-full] CP rank {c}: oracle on {rows.size} rows x {len(heads)} heads")
+        o, l, dq = O.share_rows(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, c, scale, rows, heads, want_dq=True)
+        H.compare_bf16(f"out cp{c}", H.bf16_to_np(back["out"][a])[rows][:, heads], o)
+        H.compare_lse(f"lse cp{c}", lse_cp[a][rows][:, heads].T, l)
+        H.compare_bf16(f"dq cp{c}", H.bf16_to_np(back["dq"][a])[rows][:, heads], dq)
+        # the own shard's dK / dV: both CP ranks' queries of the group contribute
+        keys = np.arange(tl_cp - 3, tl_cp)
+        kvh = [3, 30]
+        ref_k = ref_v = 0
+        for r in range(A):
+            k_, v_ = O.share_keys_dkdv(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, c, keys, kvh)
+            ref_k, ref_v = ref_k + k_, ref_v + v_
+        H.compare_bf16(f"dk cp{c}", H.bf16_to_np(back["dk"][a])[keys][:, kvh], ref_k)
+        H.compare_bf16(f"dv cp{c}", H.bf16_to_np(back["dv"][a])[keys][:, kvh], ref_v)
+    m_p.close()
+    m_cp.close()
