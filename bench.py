@@ -649,6 +649,7 @@ def main():
     step_pairs = api.step_pairs(meta)
     pairs = sum(step_pairs)
     flops_step = 14 * d * hq * pairs
+    valid_rows = int(meta.summary.valid_rows)
     stream = torch.cuda.current_stream()
     if args.phases > 0:
         sink = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -705,10 +706,10 @@ def main():
     log(f"[bench] {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
     # algorithmic HBM bytes per launch of the HBM-bound kernels: bwd_pre reads
-    # dO and out (bf16) and the LSE and writes two fp32 planes; dq_finalize reads
-    # the fp32 accumulator and writes bf16 dQ; tail_zero writes the tail rows of
-    # dQ and of every dK / dV part
-    hbm_bytes = {"bwd_pre": T_local * hq * (4 * d + 12), "dq_finalize": T_local * hq * 6 * d,
+    # dO and out (bf16) and the LSE and writes two fp32 planes; dq_pad_rows
+    # writes the padding rows of dQ; tail_zero writes the tail rows of dQ and
+    # of every dK / dV part
+    hbm_bytes = {"bwd_pre": T_local * hq * (4 * d + 12), "dq_pad_rows": (T_local - valid_rows) * hq * 2 * d,
                  "tail_zero": 2 * (t_alloc - T_local) * (hq + 2 * cp * hkv) * d}
     kernels = {}
     for name, (ms, n) in per_kernel.items():

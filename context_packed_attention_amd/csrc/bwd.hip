@@ -18,28 +18,22 @@
 
 namespace cpattn {
 
+// What both backward kernels share; the per-step shards and outputs come in
+// DkdvSteps / DqSteps.
 struct BwdParams {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
   const uint16_t* dout;
   const float* lse2;  // forward LSE in exp2 units, fp32 [hq, ld_ldv] (+inf on padding rows)
   const float* negd;  // -D = -rowsum(dO * out), fp32 [hq, ld_ldv] (0 on padding rows)
   long long ld_ldv;
-  const int32_t* q_start;
-  const int32_t* q_len;
-  const int32_t* kv_start;
-  const int32_t* kv_len;
+  const int32_t* steps;  // every step's sequence tables: [step][q_start, q_len, kv_start, kv_len][B]
+  int B;
   const int32_t* slot;   // cu_seqlens_padded / CP (slot starts, B + 1)
-  const int32_t* items;  // (sequence, tile) pairs
+  const int32_t* items;  // dQ work items: (sequence, 128-row tile) of the causal step's rows
   int hq, hkv, group;
   long long ld_q, ld_kv;
   float scale, c_log2;
-  int causal;
-  float* dq_acc;   // fp32 [T_local, hq, D]
-  int dq_first;    // 1: store, 0: accumulate
-  uint16_t* dk;    // bf16 [t_alloc, hkv, D] part of the source shard
-  uint16_t* dv;
+  uint16_t* dq;          // bf16 [t_alloc, hq, D]
 };
 
 // Per (head, local row): the forward's LSE in exp2 units and
@@ -78,14 +72,29 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
   }
 }
 
-// dQ of one ring step. Block = NWAVES wavefronts x 32 query rows of one head;
-// key tiles of 64 rows: K and V are copied straight into padded LDS tiles
-// (double-buffered). Row-major reads of K and V feed the transposed scores
-// S^T = K Q^T and dP^T = V dO^T (lane = one query row); transposing reads of
-// the same K tile feed dQ^T = K^T dS^T. Keys past the step's key range read as
-// zeros, so their K^T rows contribute nothing and need no mask.
+// The ring steps' K / V shards for the dQ kernel: step i reads shard
+// k[i] / v[i] through step i's sequence tables.
+struct DqSteps {
+  const uint16_t* k[CP_ATTN_MAX_CP];
+  const uint16_t* v[CP_ATTN_MAX_CP];
+  int kind[CP_ATTN_MAX_CP];
+  int n;
+};
+
+// dQ of every ring step at once: dQ = scale sum_i dS_i K_i summed over the
+// steps in registers, written once in bf16. Block = NWAVES wavefronts x 32
+// query rows of one head (a 128-row tile of the rows the causal step covers,
+// which are all the valid rows of the sequence's slot). The block walks the
+// steps' key ranges in one pipeline of 64-key tiles: K and V are copied
+// straight into padded LDS tiles (double-buffered, the next tile's copy may
+// belong to the next step). Row-major reads of K and V feed the transposed
+// scores S^T = K Q^T and dP^T = V dO^T (lane = one query row); transposing
+// reads of the same K tile feed dQ^T = K^T dS^T. A step that covers only the
+// second chunk's rows (s > rank) leaves the other rows out through their
+// LSE (+inf: their probabilities vanish). Keys past a step's key range read
+// as zeros, so their K^T rows contribute nothing and need no mask.
 template <int D>
-__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdParams p, DqSteps st) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
   using KCopy = TileCopy<D, false, BN, NWAVES, true>;  // K read both ways: permuted rows (V too, same plan)
@@ -98,27 +107,28 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   int item, head;
   map_block(blockIdx.x, p.hq, item, head);
   const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
-  const int qs = p.q_start[sb], ql = p.q_len[sb], kvs = p.kv_start[sb], kl = p.kv_len[sb];
+  const int B = p.B;
+  // step tables: [step][q_start, q_len, kv_start, kv_len][sequence]
+  auto tab = [&](int i, int f) { return p.steps[(long long)i * 4 * B + f * B + sb]; };
+  const int base = tab(0, 0), ql0 = tab(0, 1);  // the causal step covers every valid row of the slot
   const int q0 = tile * BM;
-  const int nq = min(BM, ql - q0);
+  const int nq = min(BM, ql0 - q0);
   const int kvh = head / p.group;
-  const int n_keys = p.causal ? min(kl, q0 + nq) : kl;
-  const int nt = (n_keys + BN - 1) / BN;
   const float c = p.c_log2;
 
-  const int qrow = q0 + w * 32 + l32;
-  const bool qok = qrow < ql;
+  const int qrow = q0 + w * 32 + l32;  // relative to the slot
+  const bool qok = qrow < ql0;
   bf16x8_t qf[NKK], df[NKK];
   {
-    const long long roff = (long long)(qs + (qok ? qrow : 0)) * p.ld_q + head * D + g * 8;
+    const long long roff = (long long)(base + (qok ? qrow : 0)) * p.ld_q + head * D + g * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       qf[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p.q + roff + kk * 16) : make_uint4(0, 0, 0, 0));
       df[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p.dout + roff + kk * 16) : make_uint4(0, 0, 0, 0));
     }
   }
-  const long long li = (long long)head * p.ld_ldv + qs + qrow;
-  const float lse2 = qok ? p.lse2[li] : __builtin_huge_valf();
+  const long long li = (long long)head * p.ld_ldv + base + qrow;
+  const float lse2_row = qok ? p.lse2[li] : __builtin_huge_valf();
   const float dq_d = qok ? -p.negd[li] : 0.f;
 
   f32x16_t acc[NMD];
@@ -131,30 +141,64 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   for (int j = 0; j < 16; ++j) negd16[j] = -dq_d;
 
   const int ldb = (int)(p.ld_kv * 2);
-  const long long kv_end = (long long)kl * ldb;
-  const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
-  const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
   KCopy kc;
   kc.init(ldb, w, lane);
-  auto issue = [&](int kt, int buf) {
-    const long long off = (long long)kt * BN * ldb;
-    kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
-    kc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
+  // a step's view for this block: its rows (slot-relative [rlo, rhi)), its
+  // keys, and how many 64-key tiles the block visits (0: the step does not
+  // reach the block's rows)
+  struct View {
+    int rlo, rhi, kl, nt, causal;
+    const uint16_t* kb;
+    const uint16_t* vb;
   };
-  if (nt > 0) issue(0, 0);
-
+  auto view = [&](int i) {
+    View v;
+    v.rlo = tab(i, 0) - base;
+    v.rhi = v.rlo + tab(i, 1);
+    v.kl = tab(i, 3);
+    v.causal = st.kind[i] == 0;
+    const int lo = max(q0, v.rlo), hi = min(q0 + nq, v.rhi);
+    const int n_keys = hi <= lo ? 0 : (v.causal ? min(v.kl, q0 + nq) : v.kl);
+    v.nt = (n_keys + BN - 1) / BN;
+    const long long kvs = tab(i, 2);
+    v.kb = st.k[i] + kvs * p.ld_kv + kvh * D;
+    v.vb = st.v[i] + kvs * p.ld_kv + kvh * D;
+    return v;
+  };
+  auto issue = [&](const View& v, int kt, int buf) {
+    const long long off = (long long)kt * BN * ldb, end = (long long)v.kl * ldb;
+    kc.copy(rsrc_from(v.kb, off, end), Ks[buf], w);
+    kc.copy(rsrc_from(v.vb, off, end), Vs[buf], w);
+  };
+  // the first step with work, then (step, tile) in order
+  int i = 0;
+  View cur = view(0);
+  while (cur.nt == 0 && i + 1 < st.n) cur = view(++i);
+  if (cur.nt > 0) issue(cur, 0, 0);
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
-  for (int kt = 0; kt < nt; ++kt) {
-    const int buf = kt & 1;
+  int kt = 0, it = 0;
+  while (cur.nt > 0) {
+    // the tile after this one, possibly the next step's first
+    int ni = i, nkt = kt + 1;
+    View nxt = cur;
+    if (nkt >= cur.nt) {
+      nkt = 0;
+      nxt.nt = 0;
+      while (nxt.nt == 0 && ni + 1 < st.n) nxt = view(++ni);
+    }
+    const bool more = nxt.nt > 0;
+    const int buf = it & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int k0 = kt * BN;
-    const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
+    const bool active = !(cur.causal && k0 > wrow_hi) && wrow_lo < min(ql0, cur.rhi) && wrow_hi >= cur.rlo;
     // the next tile's copy is issued after this tile's score products (the
     // address arithmetic then fills the wait for their results); idle
     // wavefronts issue their share at once
-    if (!active && kt + 1 < nt) issue(kt + 1, buf ^ 1);
+    if (!active && more) issue(nxt, nkt, buf ^ 1);
     if (active) {
+      // rows outside this step's query range take no part in it
+      const float lse2 = (qrow >= cur.rlo && qrow < cur.rhi) ? lse2_row : __builtin_huge_valf();
       f32x16_t s[2], dp[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -167,8 +211,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
         for (int mb = 0; mb < 2; ++mb)
           s[mb] = mfma32x32x16(lds_read_row<D, true>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
       }
-      if (kt + 1 < nt) issue(kt + 1, buf ^ 1);
-      if (p.causal && k0 + BN - 1 > wrow_lo) {
+      if (more) issue(nxt, nkt, buf ^ 1);
+      if (cur.causal && k0 + BN - 1 > wrow_lo) {
         // keys after the lane's row (a real branch, kept out of
         // if-conversion; only the tiles on a wavefront's diagonal take it)
         __asm__ volatile("" ::: "memory");
@@ -204,24 +248,21 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
           acc[md] = mfma32x32x16(lds_read_tr<D, false, true>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
       }
     }
+    i = ni;
+    kt = nkt;
+    cur = nxt;
+    ++it;
   }
   if (qok) {
-    float* dst = p.dq_acc + (long long)(qs + qrow) * p.hq * D + head * D + g * 4;
+    uint16_t* dst = p.dq + (long long)(base + qrow) * p.hq * D + head * D + g * 4;
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float4 val = make_float4(acc[md][4 * jj] * p.scale, acc[md][4 * jj + 1] * p.scale,
-                                 acc[md][4 * jj + 2] * p.scale, acc[md][4 * jj + 3] * p.scale);
-        float4* ptr = reinterpret_cast<float4*>(dst + md * 32 + jj * 8);
-        if (!p.dq_first) {
-          const float4 old = *ptr;
-          val.x += old.x;
-          val.y += old.y;
-          val.z += old.z;
-          val.w += old.w;
-        }
-        *ptr = val;
+        uint2 pk;
+        pk.x = pack2_bf16(acc[md][4 * jj] * p.scale, acc[md][4 * jj + 1] * p.scale);
+        pk.y = pack2_bf16(acc[md][4 * jj + 2] * p.scale, acc[md][4 * jj + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dst + md * 32 + jj * 8) = pk;
       }
   }
 }
@@ -239,9 +280,24 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
 // rows past the key range are computed but written as zeros. Rows of the part
 // outside the step's key range are written as zeros too, so the whole
 // shard-s part is defined.
+// The ring steps' shards and outputs for the dK/dV kernel: blocks
+// [off[i], off[i + 1]) work on step i (K / V shard k[i] / v[i], its part
+// dk[i] / dv[i], work items items[i]).
+struct DkdvSteps {
+  const uint16_t* k[CP_ATTN_MAX_CP];
+  const uint16_t* v[CP_ATTN_MAX_CP];
+  uint16_t* dk[CP_ATTN_MAX_CP];
+  uint16_t* dv[CP_ATTN_MAX_CP];
+  const int32_t* items[CP_ATTN_MAX_CP];
+  int step[CP_ATTN_MAX_CP];  // ring step index (its sequence tables)
+  int kind[CP_ATTN_MAX_CP];
+  int off[CP_ATTN_MAX_CP + 1];
+  int n;
+};
+
 template <int D, bool BIG>
 __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 / NWAVES / DKDV_KB : 1)
-    bwd_dkdv_kernel(BwdParams p) {
+    bwd_dkdv_kernel(BwdParams p, DkdvSteps sts) {
   constexpr int KB = DKDV_KB;
   constexpr int BK = DKDV_BN, BQ = 32;
   constexpr int NKK = D / 16, NMD = D / 32;
@@ -259,10 +315,16 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
+  // this block's ring step (every block of one step shares it)
+  int si = 0;
+  while (si + 1 < sts.n && (int)blockIdx.x >= sts.off[si + 1]) ++si;
+  si = __builtin_amdgcn_readfirstlane(si);
+  const int32_t* tabs = p.steps + (long long)sts.step[si] * 4 * p.B;
+  const bool causal = sts.kind[si] == 0;
   int item, kvh;
-  map_block(blockIdx.x, p.hkv, item, kvh);
-  const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
-  const int qs = p.q_start[sb], ql = p.q_len[sb], kvs = p.kv_start[sb], kl = p.kv_len[sb];
+  map_block((int)blockIdx.x - sts.off[si], p.hkv, item, kvh);
+  const int sb = sts.items[si][2 * item], tile = sts.items[si][2 * item + 1];
+  const int qs = tabs[sb], ql = tabs[p.B + sb], kvs = tabs[2 * p.B + sb], kl = tabs[3 * p.B + sb];
   const int slot_len = p.slot[sb + 1] - p.slot[sb];
   const int k0 = tile * BK;
   const int rows_here = min(BK, slot_len - k0);
@@ -280,7 +342,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     }
 
   // query tiles to visit: causal steps skip tiles entirely before this key tile
-  const int qt_begin = (p.causal && nk > 0) ? (k0 / BQ) : 0;
+  const int qt_begin = (causal && nk > 0) ? (k0 / BQ) : 0;
   const int qt_end = nk > 0 ? (ql + BQ - 1) / BQ : 0;
   const int n_qt = max(0, qt_end - qt_begin);
   const int n_iter = n_qt * p.group;
@@ -295,13 +357,13 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
       const long long off = (long long)(kvs + (ok ? key : 0)) * p.ld_kv + kvh * D + g * 8;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        kf[kb][kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(p.k + off + kk * 16) : make_uint4(0, 0, 0, 0));
+        kf[kb][kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(sts.k[si] + off + kk * 16) : make_uint4(0, 0, 0, 0));
     }
     {
       const int ldkv = (int)(p.ld_kv * 2);
       VCopy vcp;
       vcp.init(ldkv, w, lane);
-      vcp.copy(rsrc_from(p.v + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, (long long)nk * ldkv), Vt, w);
+      vcp.copy(rsrc_from(sts.v[si] + (long long)(kvs + k0) * p.ld_kv + kvh * D, 0, (long long)nk * ldkv), Vt, w);
     }
     const int ldb = (int)(p.ld_q * 2);
     const long long q_end = (long long)ql * ldb, ld_end = (long long)ql * 4;
@@ -398,7 +460,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
           tq0[md] = lds_read_tr<D, false, true>(Qs[buf], 0, md * 32, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (p.causal && qlo < wkey_hi) {
+        if (causal && qlo < wkey_hi) {
           // query rows before a lane's key (a real branch, kept out of
           // if-conversion; only a wavefront's first tiles take it)
           __asm__ volatile("" ::: "memory");
@@ -455,8 +517,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
     if (r < rows_here) {
       const int key = k0 + r;
       const bool ok = key < kl;
-      uint16_t* dkr = p.dk + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
-      uint16_t* dvr = p.dv + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+      uint16_t* dkr = sts.dk[si] + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+      uint16_t* dvr = sts.dv[si] + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
 #pragma unroll
       for (int md = 0; md < NMD; ++md)
 #pragma unroll
@@ -478,20 +540,16 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
   }
 }
 
-// dQ accumulator (fp32) -> bf16 dQ for every local row; padding rows 0.
-__global__ void __launch_bounds__(256) dq_finalize_kernel(const float* __restrict__ acc, const int32_t* __restrict__ rowflags,
+// dQ padding rows (no valid token; no dQ block covers them) set to 0;
+// launched only when the share has such rows.
+__global__ void __launch_bounds__(256) dq_pad_rows_kernel(const int32_t* __restrict__ rowflags,
                                                           uint16_t* __restrict__ dq, int t_local, int hq, int d) {
-  const long long per_row = (long long)hq * d / 4;
-  const long long n = (long long)t_local * per_row;
+  const long long u_per_row = (long long)hq * d / 8;  // 16-byte units
+  const long long n = (long long)t_local * u_per_row;
   for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
-    const int t = (int)(e / per_row);
-    uint2 pk = make_uint2(0, 0);
-    if (rowflags[t] & RF_VALID) {
-      const float4 v = *reinterpret_cast<const float4*>(acc + e * 4);
-      pk.x = pack2_bf16(v.x, v.y);
-      pk.y = pack2_bf16(v.z, v.w);
-    }
-    *reinterpret_cast<uint2*>(dq + e * 4) = pk;
+    const int t = (int)(e / u_per_row);
+    if (rowflags[t] & RF_VALID) continue;
+    reinterpret_cast<uint4*>(dq)[e] = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -520,6 +578,10 @@ __global__ void __launch_bounds__(256) tail_zero_kernel(TailPtrs ptrs, int n_ptr
     reinterpret_cast<uint4*>(base)[u] = make_uint4(0, 0, 0, 0);
   }
 }
+
+// Whether the backward runs its dK/dV launch beside its dQ launch: only when
+// the dQ launch is short (long ones measured slower with co-resident blocks).
+bool bwd_forks(const cp_attn_meta* m, int hq) { return short_launches(m->sum.tiles_fwd[0] * hq, m->device); }
 
 static unsigned grid_for(long long n, int per_block) {
   long long b = (n + per_block - 1) / per_block;
@@ -565,11 +627,9 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
   const int tl = m->sum.t_local;
   cp_attn_status rc = CP_ATTN_OK;
   if (tl > 0) {
-    const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
     const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);
-    float* dq_acc = (float*)workspace;
-    float* lse2 = (float*)((char*)workspace + o_al);
-    float* negd = (float*)((char*)workspace + o_al + l_al);
+    float* lse2 = (float*)workspace;
+    float* negd = (float*)((char*)workspace + l_al);
     const int32_t* rowflags = m->d_tab + m->lay.rowflags;
     timing_begin(st, "bwd_pre");
     hipLaunchKernelGGL(bwd_pre_kernel, dim3(grid_for((long long)tl * hq * (d / 8), 256)), dim3(256), 0, st,
@@ -583,7 +643,10 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     base.lse2 = lse2;
     base.negd = negd;
     base.ld_ldv = tl;
+    base.steps = m->d_tab + m->lay.steps;
+    base.B = m->B;
     base.slot = m->d_tab + m->lay.cupl;
+    base.items = m->d_tab + m->lay.fwd_tiles;  // the causal step's (step 0) query tiles
     base.hq = hq;
     base.hkv = hkv;
     base.group = hq / hkv;
@@ -591,75 +654,85 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     base.ld_kv = (long long)hkv * d;
     base.scale = softmax_scale;
     base.c_log2 = softmax_scale * LOG2E_F;
-    base.dq_acc = dq_acc;
+    base.dq = (uint16_t*)dq;
     const bool big = (long long)tl * hq * d * 2 >= (1ll << 31);  // local query tensors of 2 GiB or more
-    // The dK/dV launches of all ring steps are independent of the dQ launches
-    // (different outputs; both read what bwd_pre wrote). Short launches leave
-    // tails a concurrent chain can fill: then dK/dV runs on a side stream
-    // forked from the caller's; long launches stay on one stream (co-resident
+    // dK/dV of every ring step in one launch (each step writes its own part),
+    // and dQ of every step in one launch (each block sums its rows' steps in
+    // registers). The two launches are independent (both read what bwd_pre
+    // wrote): short ones run concurrently, the dK/dV one on a side stream
+    // forked from the caller's; long ones stay on one stream (co-resident
     // dK/dV and dQ blocks measured slower there).
-    long long max_dq_blocks = 0;
-    for (int i = 0; i < cp; ++i) max_dq_blocks = std::max<long long>(max_dq_blocks, m->sum.tiles_fwd[i] * hq);
-    const bool fork = short_launches(max_dq_blocks, m->device);
+    DkdvSteps ks{};
+    DqSteps qs{};
+    long long nkv = 0;
+    for (int i = 0; i < cp; ++i) {
+      const int s = m->sum.step_src[i];
+      qs.k[i] = (const uint16_t*)k_shards[s];
+      qs.v[i] = (const uint16_t*)v_shards[s];
+      qs.kind[i] = m->sum.step_kind[i];
+      const long long nb = m->sum.tiles_dkdv[i] * hkv;
+      if (nb == 0) continue;
+      const int j = ks.n++;
+      ks.k[j] = qs.k[i];
+      ks.v[j] = qs.v[i];
+      ks.dk[j] = (uint16_t*)dk_parts[s];
+      ks.dv[j] = (uint16_t*)dv_parts[s];
+      ks.items[j] = m->d_tab + m->lay.dkdv_tiles + (int64_t)i * m->lay.dkdv_cap * 2;
+      ks.step[j] = i;
+      ks.kind[j] = m->sum.step_kind[i];
+      ks.off[j] = (int)nkv;
+      nkv += nb;
+    }
+    ks.off[ks.n] = (int)nkv;
+    qs.n = cp;
+    if (nkv > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
+    const long long nq = m->sum.tiles_fwd[0] * hq;
+    const bool fork = bwd_forks(m, hq);
     SideSet* side = nullptr;
     hipStream_t sk = st;
-    if (fork) {
+    if (fork && nkv > 0) {
       if ((rc = side_set(m->device, &side)) != CP_ATTN_OK) return rc;
       sk = side->s[0];
       if ((rc = fork_to(side, st, 1)) != CP_ATTN_OK) return rc;
     }
     cp_attn_status lrc = CP_ATTN_OK;  // launch errors wait for the join
-    for (int i = 0; i < cp && lrc == CP_ATTN_OK; ++i) {
-      const int s = m->sum.step_src[i];
-      StepTab tb = step_tab(m, i);
-      BwdParams p = base;
-      p.k = (const uint16_t*)k_shards[s];
-      p.v = (const uint16_t*)v_shards[s];
-      p.q_start = tb.q_start;
-      p.q_len = tb.q_len;
-      p.kv_start = tb.kv_start;
-      p.kv_len = tb.kv_len;
-      p.causal = m->sum.step_kind[i] == 0;
-      p.dk = (uint16_t*)dk_parts[s];
-      p.dv = (uint16_t*)dv_parts[s];
-      p.dq_first = (i == 0) ? 1 : 0;
-      const long long nkv = m->sum.tiles_dkdv[i] * hkv;
-      if (nkv > 0) {
-        p.items = m->d_tab + m->lay.dkdv_tiles + (int64_t)i * m->lay.dkdv_cap * 2;
-        timing_begin(sk, "bwd_dkdv");
-        if (d == 128) {
-          if (big)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
-          else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
-        } else {
-          if (big)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
-          else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, p);
-        }
-        timing_end(sk);
-        if ((lrc = hip_check(hipGetLastError(), "bwd_dkdv launch")) != CP_ATTN_OK) break;
+    if (nkv > 0) {
+      timing_begin(sk, "bwd_dkdv");
+      if (d == 128) {
+        if (big)
+          hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, base, ks);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, base, ks);
+      } else {
+        if (big)
+          hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, base, ks);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), dim3((unsigned)nkv), dim3(BLOCK_THREADS), 0, sk, base, ks);
       }
-      const long long nq = m->sum.tiles_fwd[i] * hq;
-      if (nq > 0) {
-        p.items = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
+      timing_end(sk);
+      lrc = hip_check(hipGetLastError(), "bwd_dkdv launch");
+    }
+    if (lrc == CP_ATTN_OK && nq > 0) {
+      if (nq > 0x7fffffffLL) lrc = fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
+      else {
         timing_begin(st, "bwd_dq");
         if (d == 128)
-          hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(BLOCK_THREADS), 0, st, p);
+          hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(BLOCK_THREADS), 0, st, base, qs);
         else
-          hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(BLOCK_THREADS), 0, st, p);
+          hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(BLOCK_THREADS), 0, st, base, qs);
         timing_end(st);
-        if ((lrc = hip_check(hipGetLastError(), "bwd_dq launch")) != CP_ATTN_OK) break;
+        lrc = hip_check(hipGetLastError(), "bwd_dq launch");
       }
     }
-    if (fork && (rc = join_from(side, st, 1)) != CP_ATTN_OK) return rc;
+    if (side && (rc = join_from(side, st, 1)) != CP_ATTN_OK) return rc;
     if (lrc != CP_ATTN_OK) return lrc;
-    timing_begin(st, "dq_finalize");
-    hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for((long long)tl * hq * d / 4, 256)), dim3(256), 0, st, dq_acc,
-                       rowflags, (uint16_t*)dq, tl, hq, d);
-    timing_end(st);
-    if ((rc = hip_check(hipGetLastError(), "dq_finalize launch")) != CP_ATTN_OK) return rc;
+    if (m->sum.valid_rows < tl) {
+      timing_begin(st, "dq_pad_rows");
+      hipLaunchKernelGGL(dq_pad_rows_kernel, dim3(grid_for((long long)tl * hq * d / 8, 256)), dim3(256), 0, st,
+                         rowflags, (uint16_t*)dq, tl, hq, d);
+      timing_end(st);
+      if ((rc = hip_check(hipGetLastError(), "dq_pad_rows launch")) != CP_ATTN_OK) return rc;
+    }
   }
   if (m->sum.has_tail) {
     TailPtrs tp{};

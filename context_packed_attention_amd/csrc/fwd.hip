@@ -394,7 +394,7 @@ extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int
   const size_t o_al = (o + 255) & ~size_t(255);
   if (pass == 0)  // the running accumulator (out, lse), or one partial per step when the steps run concurrently
     return (fwd_forks(m, hq) ? (size_t)m->cp : 1) * (o_al + l);
-  return o_al + 2 * l;                     // dq accumulator + per-row lse and -D = -rowsum(dO * O)
+  return 2 * l;                            // per-row lse and -D = -rowsum(dO * O)
 }
 
 static cp_attn_status check_common(const cp_attn_meta* m, const void* q, const void* const* ks, const void* const* vs,

@@ -105,6 +105,9 @@ int cu_count(int device);
 // unit) leave tails that concurrent independent launches can fill
 bool short_launches(long long max_blocks, int device);
 
+// whether the backward runs its dK/dV and dQ launches concurrently (bwd.hip)
+bool bwd_forks(const cp_attn_meta* m, int hq);
+
 // per-kernel event timing (no-ops unless enabled through the C ABI)
 void timing_begin(hipStream_t st, const char* name);
 void timing_end(hipStream_t st);

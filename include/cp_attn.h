@@ -175,8 +175,12 @@ cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, const void* con
  * THD gradient tail zeroing ([I2] "Describe the bug" and "Expected
  * behavior"): rows [T_local, t_alloc) of dq and of every part are zeroed by
  * one extra launch, made only when the metadata shows such a tail exists.
- * When the steps' launches are short the dK/dV chain runs on a side stream
- * forked from `stream` beside the dQ chain and is joined back before the call
+ * Launches: one that computes D = rowsum(dout * out), one for the dK/dV of
+ * every ring step (each step writes its own part), one for the dQ of every
+ * step (each query tile sums its steps in registers and writes bf16 dQ
+ * once), one that zeroes dQ's padding rows when the share has any, and the
+ * tail zeroing. When the dQ launch is short the dK/dV launch runs on a side
+ * stream forked from `stream` beside it and is joined back before the call
  * returns its work to `stream`.
  *
  *  q, k_shards, v_shards, hq, hkv, d, softmax_scale, causal: as cp_attn_fwd
