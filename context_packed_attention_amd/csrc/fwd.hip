@@ -22,19 +22,11 @@ namespace cpattn {
 
 struct FwdParams {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const int32_t* q_start;
-  const int32_t* q_len;
-  const int32_t* kv_start;
-  const int32_t* kv_len;
-  const int32_t* items;  // (sequence, tile) pairs
+  const int32_t* steps;  // every step's sequence tables: [step][q_start, q_len, kv_start, kv_len][B]
+  int B;
   int hq, group;
   long long ld_q, ld_kv;  // elements per row
   float scale, c_log2;    // softmax scale, scale * log2(e)
-  int causal;
-  float* o;               // fp32 [rows, hq, D]: the step's partial, or the running accumulator
-  float* lse;             // fp32 [hq, ld_lse]
   long long ld_o, ld_lse;
   // epilogue: 0 = write the step's normalised partial (o, lse); 1 = fold it
   // into the accumulator (o, lse) through the log-sum-exp; 2 = fold it and
@@ -48,6 +40,22 @@ struct FwdParams {
   long long ld_lse_out;
 };
 
+// The ring steps of one launch: blocks [off[j], off[j + 1]) compute ring step
+// step[j] (kind kind[j]) against K / V shard k[j] / v[j], over its work items
+// items[j], into o[j] (fp32 [rows, hq, D]: the step's partial, or the running
+// accumulator) and lse[j] (fp32 [hq, ld_lse]).
+struct FwdSteps {
+  const uint16_t* k[CP_ATTN_MAX_CP];
+  const uint16_t* v[CP_ATTN_MAX_CP];
+  const int32_t* items[CP_ATTN_MAX_CP];
+  float* o[CP_ATTN_MAX_CP];
+  float* lse[CP_ATTN_MAX_CP];
+  int step[CP_ATTN_MAX_CP];
+  int kind[CP_ATTN_MAX_CP];
+  int off[CP_ATTN_MAX_CP + 1];
+  int n;
+};
+
 // One block = NWAVES wavefronts (FWD_BM query rows) of one head; each wavefront owns
 // 32 query rows. K and V tiles of 64 rows are copied straight from global
 // memory into padded LDS tiles (buffer loads with the lds modifier, no
@@ -59,7 +67,7 @@ struct FwdParams {
 // Rescaling is lazy: the running max only moves when a tile's max exceeds it
 // by more than 2^8 in exp2 units.
 template <int D>
-__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(FwdParams p) {
+__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(FwdParams p, FwdSteps st) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
@@ -71,14 +79,20 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
+  // this block's ring step (every block of one step shares it)
+  int si = 0;
+  while (si + 1 < st.n && (int)blockIdx.x >= st.off[si + 1]) ++si;
+  si = __builtin_amdgcn_readfirstlane(si);
+  const int32_t* tabs = p.steps + (long long)st.step[si] * 4 * p.B;
+  const bool causal = st.kind[si] == 0;
   int item, head;
-  map_block(blockIdx.x, p.hq, item, head);
-  const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
-  const int qs = p.q_start[sb], ql = p.q_len[sb], kvs = p.kv_start[sb], kl = p.kv_len[sb];
+  map_block((int)blockIdx.x - st.off[si], p.hq, item, head);
+  const int sb = st.items[si][2 * item], tile = st.items[si][2 * item + 1];
+  const int qs = tabs[sb], ql = tabs[p.B + sb], kvs = tabs[2 * p.B + sb], kl = tabs[3 * p.B + sb];
   const int q0 = tile * BM;
   const int nq = min(BM, ql - q0);
   const int kvh = head / p.group;
-  const int n_keys = p.causal ? min(kl, q0 + nq) : kl;
+  const int n_keys = causal ? min(kl, q0 + nq) : kl;
   const int nt = (n_keys + BN - 1) / BN;
   const float c = p.c_log2;
 
@@ -101,8 +115,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
 
   const int ldb = (int)(p.ld_kv * 2);
   const long long kv_end = (long long)kl * ldb;
-  const uint16_t* kbase = p.k + (long long)kvs * p.ld_kv + kvh * D;
-  const uint16_t* vbase = p.v + (long long)kvs * p.ld_kv + kvh * D;
+  const uint16_t* kbase = st.k[si] + (long long)kvs * p.ld_kv + kvh * D;
+  const uint16_t* vbase = st.v[si] + (long long)kvs * p.ld_kv + kvh * D;
   KCopy kc;
   VCopy vc;
   kc.init(ldb, w, lane);
@@ -144,7 +158,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
-          const bool ok = key < kl && (!p.causal || key <= qrow);
+          const bool ok = key < kl && (!causal || key <= qrow);
           s[mb][j] = ok ? s[mb][j] : NEG_INF_F;
         }
     }
@@ -202,8 +216,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
     const int k0 = kt * BN;
-    const bool active = !(p.causal && k0 > wrow_hi) && wrow_lo < ql;
-    const bool need_mask = (k0 + BN > kl) || (p.causal && k0 + BN - 1 > wrow_lo);
+    const bool active = !(causal && k0 > wrow_hi) && wrow_lo < ql;
+    const bool need_mask = (k0 + BN > kl) || (causal && k0 + BN - 1 > wrow_lo);
     bf16x8_t pb[4], vf[4][NMD];
     if (active) key_tile(kt, buf, need_mask, pb, vf);
     __builtin_amdgcn_s_waitcnt(0);
@@ -223,8 +237,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       lse = NEG_INF_F;
     }
     const int t = qs + qrow;  // local row
-    float* orow = p.o + (long long)t * p.ld_o + head * D + g * 4;
-    float* lrow = p.lse + (long long)head * p.ld_lse + t;
+    float* orow = st.o[si] + (long long)t * p.ld_o + head * D + g * 4;
+    float* lrow = st.lse[si] + (long long)head * p.ld_lse + t;
     if (p.mode == 0) {
 #pragma unroll
       for (int md = 0; md < NMD; ++md)
@@ -353,26 +367,39 @@ static bool fwd_forks(const cp_attn_meta* m, int hq) {
   return short_launches(mx, m->device);
 }
 
-static cp_attn_status launch_fwd_step(const cp_attn_meta* m, int i, const FwdParams& base, int d, int tiles,
-                                      hipStream_t st) {
-  FwdParams p = base;
-  StepTab tb = step_tab(m, i);
-  p.q_start = tb.q_start;
-  p.q_len = tb.q_len;
-  p.kv_start = tb.kv_start;
-  p.kv_len = tb.kv_len;
-  p.items = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
-  p.causal = m->sum.step_kind[i] == 0;
-  const long long blocks = (long long)tiles * p.hq;
+// One launch of the ring steps listed in `st` (their blocks one after
+// another); st.off is filled here from the steps' work-item counts.
+static cp_attn_status launch_fwd_steps(const cp_attn_meta* m, const FwdParams& p, FwdSteps st, int d,
+                                       hipStream_t strm) {
+  long long blocks = 0;
+  for (int j = 0; j < st.n; ++j) {
+    st.off[j] = (int)blocks;
+    blocks += m->sum.tiles_fwd[st.step[j]] * p.hq;
+    if (blocks > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
+  }
+  st.off[st.n] = (int)blocks;
   if (blocks == 0) return CP_ATTN_OK;
-  if (blocks > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
-  timing_begin(st, "fwd_step");
+  timing_begin(strm, "fwd_step");
   if (d == 128)
-    hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, st, p);
+    hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, strm, p, st);
   else
-    hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, st, p);
-  timing_end(st);
+    hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, strm, p, st);
+  timing_end(strm);
   return hip_check(hipGetLastError(), "fwd_step launch");
+}
+
+// Ring step i's entry of a FwdSteps list.
+static void add_step(const cp_attn_meta* m, FwdSteps& st, int i, const void* const* k_shards,
+                     const void* const* v_shards, float* o, float* lse) {
+  const int j = st.n++;
+  const int s = m->sum.step_src[i];
+  st.k[j] = (const uint16_t*)k_shards[s];
+  st.v[j] = (const uint16_t*)v_shards[s];
+  st.items[j] = m->d_tab + m->lay.fwd_tiles + (int64_t)i * m->lay.fwd_cap * 2;
+  st.o[j] = o;
+  st.lse[j] = lse;
+  st.step[j] = i;
+  st.kind[j] = m->sum.step_kind[i];
 }
 
 static unsigned stream_blocks(long long n, int per_block) {
@@ -432,7 +459,7 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   if (tl == 0) return CP_ATTN_OK;
   if ((long long)hq * d * 2 > (1ll << 20))
     return fail(CP_ATTN_ERR_UNSUPPORTED, "a row of all heads must stay within 1 MiB");
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st_ = (hipStream_t)stream;
   const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
   const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);
   char* ws = (char*)workspace;
@@ -440,6 +467,8 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
 
   FwdParams base{};
   base.q = (const uint16_t*)q;
+  base.steps = m->d_tab + m->lay.steps;
+  base.B = m->B;
   base.hq = hq;
   base.group = hq / hkv;
   base.ld_q = (long long)hq * d;
@@ -454,32 +483,25 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   base.ld_lse_out = (long long)m->t_alloc;
   const long long n4 = (long long)tl * hq * d / 4;
   if (fwd_forks(m, hq)) {
-    // step i into partial i, the steps spread over the caller's stream and
-    // side streams forked from it, then one merge of all partials
-    SideSet* side = nullptr;
-    const int nside = std::min(m->cp - 1, MAX_SIDE);
-    if ((rc = side_set(m->device, &side)) != CP_ATTN_OK) return rc;
-    if ((rc = fork_to(side, st, nside)) != CP_ATTN_OK) return rc;
+    // every step into its own partial in one launch, then one merge of all
+    // partials
+    FwdSteps st{};
     StepParts sp{};
-    cp_attn_status lrc = CP_ATTN_OK;  // launch errors wait for the join
-    for (int i = 0; i < m->cp && lrc == CP_ATTN_OK; ++i) {
-      const int s = m->sum.step_src[i];
-      FwdParams p = base;
-      p.k = (const uint16_t*)k_shards[s];
-      p.v = (const uint16_t*)v_shards[s];
-      p.o = (float*)(ws + (size_t)i * o_al);
-      p.lse = (float*)(ws + (size_t)m->cp * o_al + (size_t)i * l_al);
-      sp.o[i] = p.o;
-      sp.l[i] = p.lse;
+    for (int i = 0; i < m->cp; ++i) {
+      float* o = (float*)(ws + (size_t)i * o_al);
+      float* l = (float*)(ws + (size_t)m->cp * o_al + (size_t)i * l_al);
+      add_step(m, st, i, k_shards, v_shards, o, l);
+      sp.o[i] = o;
+      sp.l[i] = l;
       sp.kind[i] = m->sum.step_kind[i];
-      lrc = launch_fwd_step(m, i, p, d, (int)m->sum.tiles_fwd[i], i == 0 ? st : side->s[(i - 1) % nside]);
     }
-    if ((rc = join_from(side, st, nside)) != CP_ATTN_OK) return rc;
-    if (lrc != CP_ATTN_OK) return lrc;
-    timing_begin(st, "lse_merge_all");
-    hipLaunchKernelGGL(lse_merge_all_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st, sp, m->cp, rowflags,
+    FwdParams p = base;
+    p.mode = 0;
+    if ((rc = launch_fwd_steps(m, p, st, d, st_)) != CP_ATTN_OK) return rc;
+    timing_begin(st_, "lse_merge_all");
+    hipLaunchKernelGGL(lse_merge_all_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st_, sp, m->cp, rowflags,
                        (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
-    timing_end(st);
+    timing_end(st_);
     return hip_check(hipGetLastError(), "lse_merge launch");
   }
   // In order: each step folds its partial into the accumulator in its own
@@ -496,23 +518,21 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
     const int i = order[k];
     const int kind = m->sum.step_kind[i];
     FwdParams p = base;
-    p.k = (const uint16_t*)k_shards[m->sum.step_src[i]];
-    p.v = (const uint16_t*)v_shards[m->sum.step_src[i]];
-    p.o = (float*)ws;
-    p.lse = (float*)(ws + o_al);
     p.mode = (k == n_order - 1) ? 2 : 1;
     p.acc_first = acc_first;
     p.acc_second = acc_second;
-    rc = launch_fwd_step(m, i, p, d, (int)m->sum.tiles_fwd[i], st);
+    FwdSteps one{};
+    add_step(m, one, i, k_shards, v_shards, (float*)ws, (float*)(ws + o_al));
+    rc = launch_fwd_steps(m, p, one, d, st_);
     if (rc != CP_ATTN_OK) return rc;
     acc_second = true;
     if (kind != 2) acc_first = true;
   }
   if (m->sum.valid_rows < tl) {
-    timing_begin(st, "pad_rows");
-    hipLaunchKernelGGL(pad_rows_kernel, dim3(stream_blocks((long long)tl * hq * d / 8, 256)), dim3(256), 0, st,
+    timing_begin(st_, "pad_rows");
+    hipLaunchKernelGGL(pad_rows_kernel, dim3(stream_blocks((long long)tl * hq * d / 8, 256)), dim3(256), 0, st_,
                        rowflags, (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
-    timing_end(st);
+    timing_end(st_);
     rc = hip_check(hipGetLastError(), "pad_rows launch");
   }
   return rc;

@@ -142,11 +142,12 @@ size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, i
  * flash-style MFMA kernel per step, causal on local rows at step 0 only),
  * and the per-step partial outputs are folded through their log-sum-exp.
  * [I1] the P2P ring; [I2] "Describe the bug": per-step metadata. When every
- * step's launch is short (under four waves of two blocks per compute unit)
- * the steps run concurrently on side streams forked from `stream` by events
- * and joined back before one merge of all partials (the workspace then holds
- * one partial per step); otherwise they run in order on `stream`. Either way
- * the call is ordered on `stream` alone.
+ * step's launch would be short (under four waves of two blocks per compute
+ * unit) all steps run in one launch, each block computing its step's partial
+ * into that step's own buffer, and one merge of all partials follows (the
+ * workspace then holds one partial per step); otherwise the steps run in
+ * order, one launch each, each folding its partial into the accumulator in
+ * its epilogue. Everything runs on `stream`.
  *
  *  q                  bf16 [t_alloc, hq, d]: this rank's query rows
  *  k_shards, v_shards HOST arrays of CP device pointers, bf16 [t_alloc, hkv, d];

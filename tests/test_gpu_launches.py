@@ -1,9 +1,10 @@
 """Launch sequence checks (through the library's event timing, which counts
 every launch per kernel):
 
-* ring completeness: one forward kernel per ring step; each step folds its
-  partial into the accumulator in its own epilogue, or (steps run
-  concurrently) one merge of all step partials follows; the backward runs
+* ring completeness: one forward kernel per ring step, each step folding its
+  partial into the accumulator in its own epilogue, or (short steps) one
+  launch computing every step's partial and one merge of all of them; the
+  backward runs
   every step's dK/dV in one launch and every step's dQ in one launch (a CP
   path that silently drops ring steps runs fast with wrong gradients -
   "Hybrid / Hierarchical Context Parallel Skill", Pitfalls; the parity tests
@@ -52,7 +53,9 @@ def test_ring_completeness(cfg):
     for r in range(cp):
         n = _launches(bt, cp, r)
         H.log(f"[launch] cfg{cfg} rank {r}: {n}")
-        assert n["fwd_step"] == cp and n["bwd_dkdv"] == 1 and n["bwd_dq"] == 1
+        # in order: one launch per ring step; short steps: one launch for all
+        # of them and one merge of their partials
+        assert n["fwd_step"] == (1 if "lse_merge_all" in n else cp) and n["bwd_dkdv"] == 1 and n["bwd_dq"] == 1
         assert n.get("lse_merge_all", 0) in (0, 1) and (cp > 1 or "lse_merge_all" not in n)
         if "lse_merge_all" not in n:  # in order: padding rows get their own small launch
             assert ("pad_rows" in n) == (meta_valid_rows(bt, cp, r) < bt.total_rows // cp)
