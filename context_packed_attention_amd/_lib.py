@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "HINT_MISMATCH",
 
 EXPORTED = [
     "cp_attn_rank_metadata", "cp_attn_meta_summary", "cp_attn_meta_export", "cp_attn_meta_free",
-    "cp_attn_workspace_bytes", "cp_attn_fwd", "cp_attn_bwd", "cp_attn_shard_gather", "cp_attn_last_error",
+    "cp_attn_workspace_bytes", "cp_attn_fwd", "cp_attn_bwd", "cp_attn_bwd_noalloc", "cp_attn_shard_gather", "cp_attn_last_error",
     "cp_attn_timing_enable", "cp_attn_timing_read",
     "cp_attn_graph_capture", "cp_attn_graph_launch", "cp_attn_graph_kernels", "cp_attn_graph_free",
     "cp_attn_a2a_seq_to_head", "cp_attn_a2a_head_to_seq",
@@ -69,6 +69,8 @@ def load(path: str | None = None) -> C.CDLL:
     lib.cp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, C.c_float, i32, vp, vp, vp, vp,
                                 C.c_size_t, vp]
     lib.cp_attn_bwd.restype = st
+    lib.cp_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, C.c_float, i32, vp, vp, vp, vp]
+    lib.cp_attn_bwd_noalloc.restype = st
     lib.cp_attn_shard_gather.argtypes = [vp, i32, vp, vp, C.c_size_t, vp]
     lib.cp_attn_shard_gather.restype = st
     lib.cp_attn_timing_enable.argtypes = [i32]

@@ -193,6 +193,17 @@ def cp_attn_bwd(meta: Meta, q, k_shards, v_shards, out, lse, dout, hq: int, hkv:
     _check(rc, "cp_attn_bwd")
 
 
+def cp_attn_bwd_noalloc(meta: Meta, q, k_shards, v_shards, out, lse, dout, hq: int, hkv: int, d: int,
+                        softmax_scale: float, causal: int, dq, dk_parts, dv_parts, stream=None):
+    """cp_attn_bwd with no workspace: the library's fixed scratch array."""
+    _check_fwd(meta, q, k_shards, v_shards, hq, hkv, d, out, lse)
+    _check_bwd(meta, hq, hkv, d, dout, dq, dk_parts, dv_parts)
+    rc = L.load().cp_attn_bwd_noalloc(meta.handle, _ptr(q), _ptr_array(k_shards), _ptr_array(v_shards), _ptr(out),
+                                      _ptr(lse), _ptr(dout), hq, hkv, d, float(softmax_scale), int(causal), _ptr(dq),
+                                      _ptr_array(dk_parts), _ptr_array(dv_parts), _stream(stream))
+    _check(rc, "cp_attn_bwd_noalloc")
+
+
 def cp_attn_shard_gather(meta: Meta, shard: int, global_rows, local_rows, row_bytes: int, stream=None):
     _need(global_rows, "global_rows", meta.t_global * row_bytes)
     _need(local_rows, "local_rows", meta.t_local * row_bytes)

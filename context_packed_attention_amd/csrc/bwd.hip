@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "internal.h"
 #include "kern_common.h"
@@ -593,12 +595,20 @@ static unsigned grid_for(long long n, int per_block) {
 
 using namespace cpattn;
 
-extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, const void* const* k_shards,
-                                      const void* const* v_shards, const void* out, const float* lse,
-                                      const void* dout, int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
-                                      int32_t causal, void* dq, void* const* dk_parts, void* const* dv_parts,
-                                      void* workspace, size_t ws_bytes, void* stream) {
-  set_error("");
+// The backward of both entry points. ws: the per-row planes (lse in exp2
+// units, -D), cp_attn_workspace_bytes(.., 1) bytes, already checked by the
+// caller; may_fork: whether short launches may run on a side stream.
+static cp_attn_status bwd_run(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                              const void* const* v_shards, const void* out, const float* lse, const void* dout,
+                              int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* dq,
+                              void* const* dk_parts, void* const* dv_parts, void* workspace, void* stream,
+                              bool may_fork);
+
+// Argument checks shared by both entry points (before any launch).
+static cp_attn_status bwd_check(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                                const void* const* v_shards, const void* out, const float* lse, const void* dout,
+                                int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal, void* dq,
+                                void* const* dk_parts, void* const* dv_parts) {
   if (!m) return fail(CP_ATTN_ERR_INVALID_ARG, "meta is NULL");
   if (!q || !k_shards || !v_shards || !out || !lse || !dout || !dq || !dk_parts || !dv_parts)
     return fail(CP_ATTN_ERR_INVALID_ARG, "NULL tensor argument");
@@ -615,14 +625,36 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     al |= (uintptr_t)k_shards[s] | (uintptr_t)v_shards[s] | (uintptr_t)dk_parts[s] | (uintptr_t)dv_parts[s];
   }
   if (al & 15) return fail(CP_ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-  const size_t need = cp_attn_workspace_bytes(m, hq, hkv, d, 1);
-  if (!workspace || ws_bytes < need) return fail(CP_ATTN_ERR_WORKSPACE, "backward workspace missing or too small");
-  if (((uintptr_t)workspace) & 255) return fail(CP_ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != m->device)
     return fail(CP_ATTN_ERR_INVALID_ARG, "current device differs from the metadata's device");
   if ((long long)hq * d * 2 > (1ll << 20))
     return fail(CP_ATTN_ERR_UNSUPPORTED, "a row of all heads must stay within 1 MiB");
+  return CP_ATTN_OK;
+}
+
+extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                                      const void* const* v_shards, const void* out, const float* lse,
+                                      const void* dout, int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
+                                      int32_t causal, void* dq, void* const* dk_parts, void* const* dv_parts,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  set_error("");
+  cp_attn_status rc = bwd_check(m, q, k_shards, v_shards, out, lse, dout, hq, hkv, d, softmax_scale, causal, dq,
+                                dk_parts, dv_parts);
+  if (rc != CP_ATTN_OK) return rc;
+  const size_t need = cp_attn_workspace_bytes(m, hq, hkv, d, 1);
+  if (!workspace || ws_bytes < need) return fail(CP_ATTN_ERR_WORKSPACE, "backward workspace missing or too small");
+  if (((uintptr_t)workspace) & 255) return fail(CP_ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return bwd_run(m, q, k_shards, v_shards, out, lse, dout, hq, hkv, d, softmax_scale, dq, dk_parts, dv_parts,
+                 workspace, stream, true);
+}
+
+static cp_attn_status bwd_run(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                              const void* const* v_shards, const void* out, const float* lse, const void* dout,
+                              int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* dq,
+                              void* const* dk_parts, void* const* dv_parts, void* workspace, void* stream,
+                              bool may_fork) {
+  const int cp = m->cp;
   hipStream_t st = (hipStream_t)stream;
   const int tl = m->sum.t_local;
   cp_attn_status rc = CP_ATTN_OK;
@@ -687,7 +719,7 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     qs.n = cp;
     if (nkv > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
     const long long nq = m->sum.tiles_fwd[0] * hq;
-    const bool fork = bwd_forks(m, hq);
+    const bool fork = may_fork && bwd_forks(m, hq);
     SideSet* side = nullptr;
     hipStream_t sk = st;
     if (fork && nkv > 0) {
@@ -750,4 +782,59 @@ extern "C" cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, cons
     rc = hip_check(hipGetLastError(), "tail_zero launch");
   }
   return rc;
+}
+
+// ------------------------------------------------ allocation-free backward
+// cp_attn_bwd_noalloc takes its per-row planes (the only scratch the
+// backward needs: lse in exp2 units and -D, 8 * hq * T_local bytes) from a
+// fixed device array instead of a caller's workspace, for callers that
+// cannot allocate. Each GPU holds its own copy of the array for the life of
+// the process; its device address is looked up once per device (the array's
+// name in host code is a host-side stand-in, not a device address) and only
+// that address is handed to kernels. Every call on one GPU uses the same
+// array: calls that overlap on one GPU race. Nothing in it has to start at
+// zero (bwd_pre writes every row it holds before the other kernels read it).
+namespace cpattn {
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(32) << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+static std::atomic<void*> g_scratch_ptr[64];
+static std::mutex g_scratch_mu;
+
+// The array's address on the current device (looked up on first use).
+static cp_attn_status scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= 64) return fail(CP_ATTN_ERR_INVALID_ARG, "device index out of range");
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      cp_attn_status rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+      if (rc != CP_ATTN_OK) return rc;
+      if (!p) return fail(CP_ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CP_ATTN_OK;
+}
+}  // namespace cpattn
+
+extern "C" cp_attn_status cp_attn_bwd_noalloc(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                                              const void* const* v_shards, const void* out, const float* lse,
+                                              const void* dout, int32_t hq, int32_t hkv, int32_t d,
+                                              float softmax_scale, int32_t causal, void* dq, void* const* dk_parts,
+                                              void* const* dv_parts, void* stream) {
+  set_error("");
+  cp_attn_status rc = bwd_check(m, q, k_shards, v_shards, out, lse, dout, hq, hkv, d, softmax_scale, causal, dq,
+                                dk_parts, dv_parts);
+  if (rc != CP_ATTN_OK) return rc;
+  const size_t need = cp_attn_workspace_bytes(m, hq, hkv, d, 1);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(CP_ATTN_ERR_WORKSPACE, "share too large for the allocation-free backward: needs " +
+                                           std::to_string(need) + " bytes of scratch, the fixed array holds " +
+                                           std::to_string(NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((rc = scratch_on(m->device, &ws)) != CP_ATTN_OK) return rc;
+  return bwd_run(m, q, k_shards, v_shards, out, lse, dout, hq, hkv, d, softmax_scale, dq, dk_parts, dv_parts, ws,
+                 stream, false);
 }

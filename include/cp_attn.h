@@ -200,6 +200,24 @@ cp_attn_status cp_attn_bwd(const cp_attn_meta* m, const void* q, const void* con
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * cp_attn_bwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture that may not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation). The backward's only
+ * scratch (two fp32 planes per query head and local row: 8 * hq * T_local
+ * bytes) comes from a fixed device array of 32 MiB that every GPU the
+ * library runs on holds until the process ends; the call makes no
+ * allocation of any kind, and it never forks (everything runs on `stream`).
+ * Calls that overlap on one GPU race on that array: order them (one stream,
+ * or events). Errors: as cp_attn_bwd, and CP_ATTN_ERR_WORKSPACE (before any
+ * launch) when 8 * hq * T_local exceeds 32 MiB, with the sizes in
+ * cp_attn_last_error(). Other arguments and results: as cp_attn_bwd.
+ */
+cp_attn_status cp_attn_bwd_noalloc(const cp_attn_meta* m, const void* q, const void* const* k_shards,
+                                   const void* const* v_shards, const void* out, const float* lse, const void* dout,
+                                   int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal,
+                                   void* dq, void* const* dk_parts, void* const* dv_parts, void* stream);
+
+/*
  * Data-loader helper: gather the rows that rank `shard` holds out of a global
  * packed tensor (rows in cu_seqlens_padded order) into that rank's local
  * layout (see the conventions above). row_bytes = heads * head_dim * element
