@@ -702,6 +702,15 @@ static cp_attn_status bwd_run(const cp_attn_meta* m, const void* q, const void* 
       qs.k[i] = (const uint16_t*)k_shards[s];
       qs.v[i] = (const uint16_t*)v_shards[s];
       qs.kind[i] = m->sum.step_kind[i];
+    }
+    // the dK/dV launch dispatches the causal step's work items last: the
+    // other steps' blocks all sweep the whole query range from its end, so
+    // the ones running together read the same Q / dO tiles (shared in L2);
+    // the causal step's sweeps have different lengths and would put them out
+    // of step if its blocks came first
+    for (int k = 0; k < cp; ++k) {
+      const int i = (k + 1) % cp;  // steps 1 .. CP-1, then the causal step 0
+      const int s = m->sum.step_src[i];
       const long long nb = m->sum.tiles_dkdv[i] * hkv;
       if (nb == 0) continue;
       const int j = ks.n++;
