@@ -60,8 +60,8 @@ def measured_traffic(kernel, workload):
 
 
 # algorithmic flops per causal pair per query head, in units of head_dim
-ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_dkdv": 8, "bwd_dq": 2}
-EXEC_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_dkdv": 8, "bwd_dq": 6}
+ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "fwd_fused": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+EXEC_FLOPS_PER_PAIR = {"fwd_step": 4, "fwd_fused": 4, "bwd_dkdv": 8, "bwd_dq": 6}
 
 
 def log(msg):

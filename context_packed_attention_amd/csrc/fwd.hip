@@ -1,5 +1,5 @@
-// Forward of one CP rank's share: one flash-style MFMA kernel per ring step,
-// then a log-sum-exp merge of the step partials.
+// Forward of one CP rank's share: flash-style MFMA kernels over the ring
+// steps, with the log-sum-exp merge of the steps' partials.
 //
 // "thd format is not supported with hierarchical CP implementation yet": the
 // P2P ring delivers one KV shard per step and long sequences keep the ring's
@@ -10,6 +10,11 @@
 // through its first chunk; a shard from a later rank is seen in full by the
 // second query chunk only. The merge is the exact softmax identity
 //   lse = log(e^la + e^lb),  O = e^(la-lse) Oa + e^(lb-lse) Ob.
+// Long shares run one launch per step, each folding its partial into an fp32
+// accumulator in its epilogue by that identity; short shares run every step
+// in one launch whose blocks carry the online softmax's running max and sum
+// across the steps (the same identity applied key tile by key tile), so no
+// partial leaves the registers.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -66,7 +71,16 @@ struct FwdSteps {
 // the step's key range read as zeros (buffer range check) and are masked.
 // Rescaling is lazy: the running max only moves when a tile's max exceeds it
 // by more than 2^8 in exp2 units.
-template <int D>
+// FUSED = false: the block computes one ring step (entry si of the list, its
+// rows relative to that step's query range) and its epilogue writes or folds
+// that step's normalised partial (p.mode). FUSED = true: the block's rows come
+// from entry 0's work items (the causal step, which covers every valid row of
+// its sequence slot) and it runs through every entry's key tiles in turn, so
+// the online softmax carries the running max and sum from one ring step to
+// the next and the log-sum-exp merge of the steps happens in registers; the
+// epilogue writes the bf16 output and the final LSE. Rows outside an entry's
+// query range take no part in it (masked).
+template <int D, bool FUSED>
 __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(FwdParams p, FwdSteps st) {
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16;
@@ -79,24 +93,24 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
-  // this block's ring step (every block of one step shares it)
+  // this block's entry of the list (every block of one entry shares it)
   int si = 0;
-  while (si + 1 < st.n && (int)blockIdx.x >= st.off[si + 1]) ++si;
-  si = __builtin_amdgcn_readfirstlane(si);
-  const int32_t* tabs = p.steps + (long long)st.step[si] * 4 * p.B;
-  const bool causal = st.kind[si] == 0;
+  if constexpr (!FUSED) {
+    while (si + 1 < st.n && (int)blockIdx.x >= st.off[si + 1]) ++si;
+    si = __builtin_amdgcn_readfirstlane(si);
+  }
   int item, head;
   map_block((int)blockIdx.x - st.off[si], p.hq, item, head);
   const int sb = st.items[si][2 * item], tile = st.items[si][2 * item + 1];
-  const int qs = tabs[sb], ql = tabs[p.B + sb], kvs = tabs[2 * p.B + sb], kl = tabs[3 * p.B + sb];
+  // entry j's sequence tables: [step][q_start, q_len, kv_start, kv_len][B]
+  auto tab = [&](int j, int f) { return p.steps[((long long)st.step[j] * 4 + f) * p.B + sb]; };
+  const int qs = tab(si, 0), ql = tab(si, 1);  // the block's rows are relative to qs
   const int q0 = tile * BM;
   const int nq = min(BM, ql - q0);
   const int kvh = head / p.group;
-  const int n_keys = causal ? min(kl, q0 + nq) : kl;
-  const int nt = (n_keys + BN - 1) / BN;
   const float c = p.c_log2;
 
-  const int qrow = q0 + w * 32 + l32;  // relative to the step's query range
+  const int qrow = q0 + w * 32 + l32;  // relative to qs
   bf16x8_t qf[NKK];
   {
     const bool ok = qrow < ql;
@@ -114,25 +128,56 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   float m_run = NEG_INF_F, l_run = 0.f;
 
   const int ldb = (int)(p.ld_kv * 2);
-  const long long kv_end = (long long)kl * ldb;
-  const uint16_t* kbase = st.k[si] + (long long)kvs * p.ld_kv + kvh * D;
-  const uint16_t* vbase = st.v[si] + (long long)kvs * p.ld_kv + kvh * D;
+  // A position in the block's sequence of key tiles: entry j, key tile kt of
+  // its nt, with the entry's query rows [rlo, rhi) (relative to qs), keys,
+  // first key row in its shard and mask kind.
+  struct Cur {
+    int j, kt, nt, rlo, rhi, kl, kvs, causal;
+  };
+  auto at = [&](int j) {
+    Cur u;
+    u.j = j;
+    u.kt = 0;
+    u.rlo = FUSED ? tab(j, 0) - qs : 0;
+    u.rhi = FUSED ? u.rlo + tab(j, 1) : ql;
+    u.kl = tab(j, 3);
+    u.kvs = tab(j, 2);
+    u.causal = st.kind[j] == 0;
+    const int lo = max(q0, u.rlo), hi = min(q0 + nq, u.rhi);
+    const int n_keys = hi <= lo ? 0 : (u.causal ? min(u.kl, q0 + nq) : u.kl);
+    u.nt = (n_keys + BN - 1) / BN;
+    return u;
+  };
+  // on to the next key tile (FUSED: possibly the first of a later entry);
+  // false past the last
+  auto advance = [&](Cur& u) {
+    if (++u.kt < u.nt) return true;
+    if constexpr (FUSED) {
+      while (u.j + 1 < st.n) {
+        u = at(u.j + 1);
+        if (u.nt > 0) return true;
+      }
+    }
+    return false;
+  };
   KCopy kc;
   VCopy vc;
   kc.init(ldb, w, lane);
   vc.init(ldb, w, lane);
-  auto issue = [&](int kt, int buf) {
-    const long long off = (long long)kt * BN * ldb;
-    kc.copy(rsrc_from(kbase, off, kv_end), Ks[buf], w);
-    vc.copy(rsrc_from(vbase, off, kv_end), Vs[buf], w);
+  auto issue = [&](const Cur& u, int buf) {
+    const long long off = (long long)u.kt * BN * ldb, end = (long long)u.kl * ldb;
+    const long long row0 = (long long)u.kvs * p.ld_kv + kvh * D;
+    kc.copy(rsrc_from(st.k[u.j] + row0, off, end), Ks[buf], w);
+    vc.copy(rsrc_from(st.v[u.j] + row0, off, end), Vs[buf], w);
   };
 
   const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units
   // first half of a key tile: scores, V fragments, softmax, P packed to
   // bf16; masking runs only on a wavefront's last tiles (keys past the
-  // range, or at the causal step keys after its first row)
-  auto key_tile = [&](int kt, int buf, bool masked, bf16x8_t (&pb)[4], bf16x8_t (&vf)[4][NMD]) {
-    const int k0 = kt * BN;
+  // range, or at the causal step keys after its first row) and, fused, on
+  // the tiles of entries whose query range splits the wavefront's rows
+  auto key_tile = [&](const Cur& u, int buf, bool masked, bf16x8_t (&pb)[4], bf16x8_t (&vf)[4][NMD]) {
+    const int k0 = u.kt * BN;
     f32x16_t s[2];
     s[0] = zero16();
     s[1] = zero16();
@@ -153,12 +198,13 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     if (masked) {
       // a real branch (kept out of if-conversion), taken on few tiles
       __asm__ volatile("" ::: "memory");
+      const bool row_in = !FUSED || (qrow >= u.rlo && qrow < u.rhi);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
-          const bool ok = key < kl && (!causal || key <= qrow);
+          const bool ok = row_in && key < u.kl && (!u.causal || key <= qrow);
           s[mb][j] = ok ? s[mb][j] : NEG_INF_F;
         }
     }
@@ -200,30 +246,46 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       for (int md = 0; md < NMD; ++md) o[md] = mfma32x32x16(vf[kk2][md], pb[kk2], o[md]);
   };
 
-  // Tile kt's buffers are free once its scores and V fragments have been
+  // Tile it's buffers are free once its scores and V fragments have been
   // read, so the block synchronises there (not at the top of the next
-  // iteration): that barrier also publishes tile kt + 1's copy, and tile kt +
-  // 2's copy goes into the freed buffers right after it. The P V products of
-  // tile kt and the scores of tile kt + 1 then follow each other with no
-  // barrier between.
-  if (nt > 0) {
-    issue(0, 0);
+  // iteration): that barrier also publishes tile it + 1's copy, and tile
+  // it + 2's copy goes into the freed buffers right after it. The P V
+  // products of tile it and the scores of tile it + 1 then follow each other
+  // with no barrier between. `cur` walks the tiles being computed, `pre` the
+  // tiles being copied, two ahead.
+  Cur cur = at(si);
+  if constexpr (FUSED) {
+    while (cur.nt == 0 && cur.j + 1 < st.n) cur = at(cur.j + 1);
+  }
+  bool more = cur.nt > 0;
+  Cur pre = cur;
+  bool pre_more = more;
+  if (more) {
+    issue(pre, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (nt > 1) issue(1, 1);
+    pre_more = advance(pre);
+    if (pre_more) issue(pre, 1);
   }
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
-  for (int kt = 0; kt < nt; ++kt) {
-    const int buf = kt & 1;
-    const int k0 = kt * BN;
-    const bool active = !(causal && k0 > wrow_hi) && wrow_lo < ql;
-    const bool need_mask = (k0 + BN > kl) || (causal && k0 + BN - 1 > wrow_lo);
+  const int wrow_last = min(wrow_hi, ql - 1);  // the wavefront's last row with a query
+  for (int it = 0; more; ++it) {
+    const int buf = it & 1;
+    const int k0 = cur.kt * BN;
+    const bool rows_any = wrow_lo < ql && wrow_last >= cur.rlo && wrow_lo < cur.rhi;
+    const bool rows_all = wrow_lo >= cur.rlo && wrow_last < cur.rhi;
+    const bool active = rows_any && !(cur.causal && k0 > wrow_hi);
+    const bool need_mask = (k0 + BN > cur.kl) || (cur.causal && k0 + BN - 1 > wrow_lo) || !rows_all;
     bf16x8_t pb[4], vf[4][NMD];
-    if (active) key_tile(kt, buf, need_mask, pb, vf);
+    if (active) key_tile(cur, buf, need_mask, pb, vf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < nt) issue(kt + 2, buf);
+    if (pre_more) {
+      pre_more = advance(pre);
+      if (pre_more) issue(pre, buf);
+    }
     if (active) pv_tile(pb, vf);
+    more = advance(cur);
   }
 
   const float lt = sum_halves(l_run);
@@ -237,6 +299,21 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       lse = NEG_INF_F;
     }
     const int t = qs + qrow;  // local row
+    if constexpr (FUSED) {
+      // every step is in: the bf16 output and the final LSE
+      uint16_t* out_row = p.out + (long long)t * p.ld_o + head * D + g * 4;
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint2 pk;
+          pk.x = pack2_bf16(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv);
+          pk.y = pack2_bf16(o[md][4 * jj + 2] * inv, o[md][4 * jj + 3] * inv);
+          *reinterpret_cast<uint2*>(out_row + md * 32 + jj * 8) = pk;
+        }
+      if (g == 0) p.lse_out[(long long)head * p.ld_lse_out + t] = lse;
+      return;
+    }
     float* orow = st.o[si] + (long long)t * p.ld_o + head * D + g * 4;
     float* lrow = st.lse[si] + (long long)head * p.ld_lse + t;
     if (p.mode == 0) {
@@ -294,7 +371,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
 }
 
 // Padding rows of the final output: out 0, LSE -inf (every valid row is
-// written by the last ring step's epilogue).
+// written by the last ring step's epilogue, or by the fused launch).
 __global__ void __launch_bounds__(256) pad_rows_kernel(const int32_t* __restrict__ rowflags, uint16_t* __restrict__ out,
                                                        float* __restrict__ lse_out, int t_local, int hq, int d,
                                                        long long ld_lse_out) {
@@ -309,58 +386,10 @@ __global__ void __launch_bounds__(256) pad_rows_kernel(const int32_t* __restrict
   }
 }
 
-// All step partials folded at once (the launches ran concurrently, each into
-// its own buffer): for every (row, head), the log-sum-exp of the steps that
-// cover the row and the correspondingly weighted outputs; writes the bf16
-// output and the final LSE for every local row (padding rows 0 / -inf).
-struct StepParts {
-  const float* o[CP_ATTN_MAX_CP];
-  const float* l[CP_ATTN_MAX_CP];
-  int kind[CP_ATTN_MAX_CP];
-};
-
-__global__ void __launch_bounds__(256) lse_merge_all_kernel(StepParts sp, int nsteps, const int32_t* __restrict__ rowflags,
-                                                            uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                                                            int t_local, int hq, int d, long long ld_lse_out) {
-  const long long q4_per_row = (long long)hq * d / 4;
-  const long long n = (long long)t_local * q4_per_row;
-  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
-    const int t = (int)(e / q4_per_row);
-    const int off = (int)(e - (long long)t * q4_per_row) * 4;
-    const int h = off / d;
-    const int f = rowflags[t];
-    const bool valid = f & RF_VALID;
-    const long long li = (long long)h * t_local + t;
-    float m = NEG_INF_F;
-    if (valid)
-      for (int i = 0; i < nsteps; ++i)
-        if (sp.kind[i] != 2 || (f & RF_SECOND)) m = fmaxf(m, sp.l[i][li]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lse = NEG_INF_F;
-    if (m != NEG_INF_F) {
-      float ssum = 0.f;
-      for (int i = 0; i < nsteps; ++i) {
-        if (sp.kind[i] == 2 && !(f & RF_SECOND)) continue;
-        const float wgt = __expf(sp.l[i][li] - m);
-        const float4 o = *reinterpret_cast<const float4*>(sp.o[i] + (long long)t * hq * d + off);
-        ssum += wgt;
-        acc = make_float4(acc.x + wgt * o.x, acc.y + wgt * o.y, acc.z + wgt * o.z, acc.w + wgt * o.w);
-      }
-      const float inv = 1.f / ssum;
-      acc = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-      lse = m + __logf(ssum);
-    }
-    uint2 pk;
-    pk.x = pack2_bf16(acc.x, acc.y);
-    pk.y = pack2_bf16(acc.z, acc.w);
-    *reinterpret_cast<uint2*>(out + (long long)t * hq * d + off) = pk;
-    if ((off % d) == 0) lse_out[(long long)h * ld_lse_out + t] = lse;
-  }
-}
-
-// Whether the forward runs its ring steps concurrently (each into its own
-// partial buffer, merged once at the end): only for short launches.
-static bool fwd_forks(const cp_attn_meta* m, int hq) {
+// Whether the forward runs every ring step in one fused launch (each block
+// through all steps, merged in registers): when the steps' own launches
+// would be short.
+static bool fwd_fused(const cp_attn_meta* m, int hq) {
   if (m->cp < 2) return false;
   long long mx = 0;
   for (int i = 0; i < m->cp; ++i) mx = std::max<long long>(mx, m->sum.tiles_fwd[i] * hq);
@@ -368,22 +397,35 @@ static bool fwd_forks(const cp_attn_meta* m, int hq) {
 }
 
 // One launch of the ring steps listed in `st` (their blocks one after
-// another); st.off is filled here from the steps' work-item counts.
-static cp_attn_status launch_fwd_steps(const cp_attn_meta* m, const FwdParams& p, FwdSteps st, int d,
+// another; st.off is filled here from the steps' work-item counts), or
+// (fused) one launch over the work items of entry 0, every block running
+// through all the entries.
+static cp_attn_status launch_fwd_steps(const cp_attn_meta* m, const FwdParams& p, FwdSteps st, int d, bool fused,
                                        hipStream_t strm) {
   long long blocks = 0;
   for (int j = 0; j < st.n; ++j) {
     st.off[j] = (int)blocks;
-    blocks += m->sum.tiles_fwd[st.step[j]] * p.hq;
+    if (!fused || j == 0) blocks += m->sum.tiles_fwd[st.step[j]] * p.hq;
     if (blocks > 0x7fffffffLL) return fail(CP_ATTN_ERR_UNSUPPORTED, "too many work items");
   }
-  st.off[st.n] = (int)blocks;
-  if (blocks == 0) return CP_ATTN_OK;
-  timing_begin(strm, "fwd_step");
-  if (d == 128)
-    hipLaunchKernelGGL(fwd_step_kernel<128>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, strm, p, st);
+  if (fused)
+    for (int j = 0; j <= st.n; ++j) st.off[j] = 0;
   else
-    hipLaunchKernelGGL(fwd_step_kernel<64>, dim3((unsigned)blocks), dim3(BLOCK_THREADS), 0, strm, p, st);
+    st.off[st.n] = (int)blocks;
+  if (blocks == 0) return CP_ATTN_OK;
+  const dim3 grid((unsigned)blocks), blk(BLOCK_THREADS);
+  timing_begin(strm, fused ? "fwd_fused" : "fwd_step");
+  if (d == 128) {
+    if (fused)
+      hipLaunchKernelGGL((fwd_step_kernel<128, true>), grid, blk, 0, strm, p, st);
+    else
+      hipLaunchKernelGGL((fwd_step_kernel<128, false>), grid, blk, 0, strm, p, st);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((fwd_step_kernel<64, true>), grid, blk, 0, strm, p, st);
+    else
+      hipLaunchKernelGGL((fwd_step_kernel<64, false>), grid, blk, 0, strm, p, st);
+  }
   timing_end(strm);
   return hip_check(hipGetLastError(), "fwd_step launch");
 }
@@ -419,8 +461,8 @@ extern "C" size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int
   const size_t o = tl * hq * d * sizeof(float);
   const size_t l = ((tl * hq * sizeof(float)) + 255) & ~size_t(255);
   const size_t o_al = (o + 255) & ~size_t(255);
-  if (pass == 0)  // the running accumulator (out, lse), or one partial per step when the steps run concurrently
-    return (fwd_forks(m, hq) ? (size_t)m->cp : 1) * (o_al + l);
+  if (pass == 0)  // the running accumulator (out, lse); the fused launch of short shares leaves it untouched
+    return o_al + l;
   return 2 * l;                            // per-row lse and -D = -rowsum(dO * O)
 }
 
@@ -461,7 +503,6 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
     return fail(CP_ATTN_ERR_UNSUPPORTED, "a row of all heads must stay within 1 MiB");
   hipStream_t st_ = (hipStream_t)stream;
   const size_t o_al = (((size_t)tl * hq * d * sizeof(float)) + 255) & ~size_t(255);
-  const size_t l_al = (((size_t)tl * hq * sizeof(float)) + 255) & ~size_t(255);
   char* ws = (char*)workspace;
   const int32_t* rowflags = m->d_tab + m->lay.rowflags;
 
@@ -481,52 +522,38 @@ extern "C" cp_attn_status cp_attn_fwd(const cp_attn_meta* m, const void* q, cons
   base.out = (uint16_t*)out;
   base.lse_out = lse;
   base.ld_lse_out = (long long)m->t_alloc;
-  const long long n4 = (long long)tl * hq * d / 4;
-  if (fwd_forks(m, hq)) {
-    // every step into its own partial in one launch, then one merge of all
-    // partials
+  if (fwd_fused(m, hq)) {
+    // every step in one launch, the causal step first (its work items are
+    // the blocks' rows), then the others in ring order
     FwdSteps st{};
-    StepParts sp{};
-    for (int i = 0; i < m->cp; ++i) {
-      float* o = (float*)(ws + (size_t)i * o_al);
-      float* l = (float*)(ws + (size_t)m->cp * o_al + (size_t)i * l_al);
-      add_step(m, st, i, k_shards, v_shards, o, l);
-      sp.o[i] = o;
-      sp.l[i] = l;
-      sp.kind[i] = m->sum.step_kind[i];
+    for (int i = 0; i < m->cp; ++i) add_step(m, st, i, k_shards, v_shards, nullptr, nullptr);
+    FwdParams p = base;
+    p.mode = 2;
+    if ((rc = launch_fwd_steps(m, p, st, d, true, st_)) != CP_ATTN_OK) return rc;
+  } else {
+    // In order: each step folds its partial into the accumulator in its own
+    // epilogue. The steps are independent on one device, so the second-chunk
+    // steps (kind 2) run first, then the kind-1 steps, and the causal step,
+    // which covers every valid row of both chunks, runs last and writes the
+    // bf16 output and the final LSE.
+    int order[CP_ATTN_MAX_CP], n_order = 0;
+    for (int want : {2, 1, 0})
+      for (int i = 0; i < m->cp; ++i)
+        if (m->sum.step_kind[i] == want) order[n_order++] = i;
+    bool acc_first = false, acc_second = false;
+    for (int k = 0; k < n_order; ++k) {
+      const int i = order[k];
+      const int kind = m->sum.step_kind[i];
+      FwdParams p = base;
+      p.mode = (k == n_order - 1) ? 2 : 1;
+      p.acc_first = acc_first;
+      p.acc_second = acc_second;
+      FwdSteps one{};
+      add_step(m, one, i, k_shards, v_shards, (float*)ws, (float*)(ws + o_al));
+      if ((rc = launch_fwd_steps(m, p, one, d, false, st_)) != CP_ATTN_OK) return rc;
+      acc_second = true;
+      if (kind != 2) acc_first = true;
     }
-    FwdParams p = base;
-    p.mode = 0;
-    if ((rc = launch_fwd_steps(m, p, st, d, st_)) != CP_ATTN_OK) return rc;
-    timing_begin(st_, "lse_merge_all");
-    hipLaunchKernelGGL(lse_merge_all_kernel, dim3(stream_blocks(n4, 256)), dim3(256), 0, st_, sp, m->cp, rowflags,
-                       (uint16_t*)out, lse, tl, hq, d, (long long)m->t_alloc);
-    timing_end(st_);
-    return hip_check(hipGetLastError(), "lse_merge launch");
-  }
-  // In order: each step folds its partial into the accumulator in its own
-  // epilogue. The steps are independent on one device, so the second-chunk
-  // steps (kind 2) run first, then the kind-1 steps, and the causal step,
-  // which covers every valid row of both chunks, runs last and writes the
-  // bf16 output and the final LSE.
-  int order[CP_ATTN_MAX_CP], n_order = 0;
-  for (int want : {2, 1, 0})
-    for (int i = 0; i < m->cp; ++i)
-      if (m->sum.step_kind[i] == want) order[n_order++] = i;
-  bool acc_first = false, acc_second = false;
-  for (int k = 0; k < n_order; ++k) {
-    const int i = order[k];
-    const int kind = m->sum.step_kind[i];
-    FwdParams p = base;
-    p.mode = (k == n_order - 1) ? 2 : 1;
-    p.acc_first = acc_first;
-    p.acc_second = acc_second;
-    FwdSteps one{};
-    add_step(m, one, i, k_shards, v_shards, (float*)ws, (float*)(ws + o_al));
-    rc = launch_fwd_steps(m, p, one, d, st_);
-    if (rc != CP_ATTN_OK) return rc;
-    acc_second = true;
-    if (kind != 2) acc_first = true;
   }
   if (m->sum.valid_rows < tl) {
     timing_begin(st_, "pad_rows");

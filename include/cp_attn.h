@@ -130,24 +130,24 @@ cp_attn_status cp_attn_meta_export(const cp_attn_meta* m, int32_t* host_buf, siz
 /* Release the handle (synchronises the device it was built on). NULL is a no-op. */
 void cp_attn_meta_free(cp_attn_meta* m);
 
-/* Workspace bytes needed by cp_attn_fwd (pass 0) or cp_attn_bwd (pass 1);
- * 0 for a NULL handle or non-positive sizes. The forward's figure depends on
- * the launch plan (see cp_attn_fwd), so take it from this call rather than a
- * formula. */
+/* Workspace bytes needed by cp_attn_fwd (pass 0: one fp32 output accumulator
+ * and LSE plane, 4 * (hq * d + hq) * T_local bytes rounded up) or cp_attn_bwd
+ * (pass 1: two fp32 planes of hq * T_local); 0 for a NULL handle or
+ * non-positive sizes. */
 size_t cp_attn_workspace_bytes(const cp_attn_meta* m, int32_t hq, int32_t hkv, int32_t d, int32_t pass);
 
 /*
  * Forward of the rank's share: for ring step i = 0..CP-1 the step's query
- * rows attend to the step's key rows of shard s = (rank - i) mod CP (one
- * flash-style MFMA kernel per step, causal on local rows at step 0 only),
- * and the per-step partial outputs are folded through their log-sum-exp.
- * [I1] the P2P ring; [I2] "Describe the bug": per-step metadata. When every
- * step's launch would be short (under four waves of two blocks per compute
- * unit) all steps run in one launch, each block computing its step's partial
- * into that step's own buffer, and one merge of all partials follows (the
- * workspace then holds one partial per step); otherwise the steps run in
- * order, one launch each, each folding its partial into the accumulator in
- * its epilogue. Everything runs on `stream`.
+ * rows attend to the step's key rows of shard s = (rank - i) mod CP (flash-
+ * style MFMA kernels, causal on local rows at step 0 only), and the per-step
+ * partial outputs are folded through their log-sum-exp. [I1] the P2P ring;
+ * [I2] "Describe the bug": per-step metadata. When every step's own launch
+ * would be short (under four waves of two blocks per compute unit) all steps
+ * run in one launch whose blocks carry the online softmax across the steps
+ * (the fold applied tile by tile in registers; the workspace is not
+ * touched); otherwise the steps run in order, one launch each, each folding
+ * its normalised partial into the workspace's accumulator in its epilogue.
+ * Everything runs on `stream`.
  *
  *  q                  bf16 [t_alloc, hq, d]: this rank's query rows
  *  k_shards, v_shards HOST arrays of CP device pointers, bf16 [t_alloc, hkv, d];

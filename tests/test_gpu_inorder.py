@@ -38,7 +38,7 @@ def test_in_order_forward_with_padding(rank):
     api.cp_attn_timing_enable(False)
     n = {k: v[1] for k, v in api.cp_attn_timing_read().items()}
     H.log(f"[inorder] rank {rank} launches {n}")
-    assert n["fwd_step"] == CP and "lse_merge_all" not in n and n.get("pad_rows") == 1
+    assert n["fwd_step"] == CP and "fwd_fused" not in n and n.get("pad_rows") == 1
 
     own = O.shard_rows(bt.cu, bt.cup, CP, rank)
     valid = O.valid_mask(bt.cu, bt.cup)[own]

@@ -3,12 +3,11 @@ every launch per kernel):
 
 * ring completeness: one forward kernel per ring step, each step folding its
   partial into the accumulator in its own epilogue, or (short steps) one
-  launch computing every step's partial and one merge of all of them; the
-  backward runs
-  every step's dK/dV in one launch and every step's dQ in one launch (a CP
-  path that silently drops ring steps runs fast with wrong gradients -
-  "Hybrid / Hierarchical Context Parallel Skill", Pitfalls; the parity tests
-  compare every step's dK/dV part and the dQ summed over all steps);
+  fused launch whose blocks run through every step; the backward runs every
+  step's dK/dV in one launch and every step's dQ in one launch (a CP path
+  that silently drops ring steps runs fast with wrong gradients - "Hybrid /
+  Hierarchical Context Parallel Skill", Pitfalls; the parity tests compare
+  every step's dK/dV part and the dQ summed over all steps);
 * the padding decision by value gives the same launch sequence for an
   aliased, NULL or distinct-equal cu_seqlens_padded, and for an asserted
   pad_hint that agrees with the values;
@@ -53,12 +52,14 @@ def test_ring_completeness(cfg):
     for r in range(cp):
         n = _launches(bt, cp, r)
         H.log(f"[launch] cfg{cfg} rank {r}: {n}")
-        # in order: one launch per ring step; short steps: one launch for all
-        # of them and one merge of their partials
-        assert n["fwd_step"] == (1 if "lse_merge_all" in n else cp) and n["bwd_dkdv"] == 1 and n["bwd_dq"] == 1
-        assert n.get("lse_merge_all", 0) in (0, 1) and (cp > 1 or "lse_merge_all" not in n)
-        if "lse_merge_all" not in n:  # in order: padding rows get their own small launch
-            assert ("pad_rows" in n) == (meta_valid_rows(bt, cp, r) < bt.total_rows // cp)
+        # in order: one launch per ring step; short steps: one fused launch
+        if "fwd_fused" in n:
+            assert n["fwd_fused"] == 1 and "fwd_step" not in n and cp > 1
+        else:
+            assert n["fwd_step"] == cp
+        assert n["bwd_dkdv"] == 1 and n["bwd_dq"] == 1
+        # padding rows of out / LSE get their own small launch, only when present
+        assert n.get("pad_rows", 0) == int(meta_valid_rows(bt, cp, r) < bt.total_rows // cp)
         assert n["bwd_pre"] == 1
         assert n.get("dq_pad_rows", 0) == int(meta_valid_rows(bt, cp, r) < bt.total_rows // cp)
         assert "tail_zero" not in n
