@@ -82,8 +82,7 @@ struct cp_attn_meta {
   int B, cp, rank, pad_hint;
   int64_t t_alloc;
   cpattn::MetaLayout lay;
-  int32_t* d_tab;      // device tables
-  int32_t* h_summary;  // pinned [SW_COUNT]
+  int32_t* d_tab;  // device tables
   cp_attn_summary sum;
 };
 

@@ -71,22 +71,30 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 // valid rows of chunk k when L valid tokens fill chunks of size c in order
 __device__ __forceinline__ int chunk_valid(int L, int c, int k) { return clampi(L - k * c, 0, c); }
 
-// Block-wide exclusive scan over 256 threads; returns the exclusive prefix and
-// writes the block total to *total.
+// Block-wide exclusive scan over 256 threads (four wavefronts: a shuffle scan
+// within each, then the wavefront totals through LDS); returns the exclusive
+// prefix and writes the block total to *total. Two barriers; `sm` holds at
+// least 4 ints and may be reused right after the call.
 __device__ int block_excl_scan256(int v, int* sm, int* total) {
-  const int t = threadIdx.x;
-  sm[t] = v;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    int add = t >= d ? sm[t - d] : 0;
-    __syncthreads();
-    sm[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
-  int incl = sm[t];
-  *total = sm[255];
+  if (lane == 63) sm[wv] = x;
   __syncthreads();
-  return incl - v;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int w = sm[k];
+    before += k < wv ? w : 0;
+    tot += w;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
 }
 
 // One block of 256 threads. Builds every per-sequence table, the validation
@@ -154,13 +162,13 @@ __global__ void __launch_bounds__(256) meta_tables_kernel(const int32_t* __restr
       int vals[3] = {f + sc, f, sc};
       int64_t offs[3] = {L.cu_full, L.cu_first, L.cu_second};
       for (int k = 0; k < 3; ++k) {
+        // every thread reads the carry before the scan's barriers, thread 0
+        // updates it after them; the next read is in the next round of 256
         int tot;
-        int ex = block_excl_scan256(vals[k], sm, &tot);
-        int carry = cnt_carry[3 * s + k];
+        const int carry = cnt_carry[3 * s + k];
+        const int ex = block_excl_scan256(vals[k], sm, &tot);
         if (in) tabp[offs[k] + (int64_t)s * (B + 1) + b] = carry + ex;
-        __syncthreads();
         if (t == 0) cnt_carry[3 * s + k] = carry + tot;
-        __syncthreads();
       }
     }
     // step tables and per-sequence work-item counts
@@ -181,18 +189,14 @@ __global__ void __launch_bounds__(256) meta_tables_kernel(const int32_t* __restr
       int nf = in ? (q_len + FWD_BM - 1) / FWD_BM : 0;
       int nk = in ? (Pb / cp + DKDV_BN - 1) / DKDV_BN : 0;
       int tot;
+      const int carry_f = cnt_carry[3 * cp + i];
       int ex = block_excl_scan256(nf, sm, &tot);
-      int carry = cnt_carry[3 * cp + i];
-      if (in) tabp[L.fwd_off + (int64_t)i * (B + 1) + b] = carry + ex;
-      __syncthreads();
-      if (t == 0) cnt_carry[3 * cp + i] = carry + tot;
-      __syncthreads();
+      if (in) tabp[L.fwd_off + (int64_t)i * (B + 1) + b] = carry_f + ex;
+      if (t == 0) cnt_carry[3 * cp + i] = carry_f + tot;
+      const int carry_k = cnt_carry[4 * cp + i];
       ex = block_excl_scan256(nk, sm, &tot);
-      carry = cnt_carry[4 * cp + i];
-      if (in) tabp[L.dkdv_off + (int64_t)i * (B + 1) + b] = carry + ex;
-      __syncthreads();
-      if (t == 0) cnt_carry[4 * cp + i] = carry + tot;
-      __syncthreads();
+      if (in) tabp[L.dkdv_off + (int64_t)i * (B + 1) + b] = carry_k + ex;
+      if (t == 0) cnt_carry[4 * cp + i] = carry_k + tot;
     }
   }
   __syncthreads();
@@ -390,6 +394,24 @@ static std::string describe_meta_error(int e) {
   return s;
 }
 
+// Pinned landing buffer of the summary: one per calling thread and device,
+// allocated on first use and kept until the process ends (the summary is read
+// within the call that copies it, so one buffer serves every call).
+static cp_attn_status summary_buffer(int device, int32_t** out) {
+  static thread_local int32_t* buf[64] = {};
+  if (device < 0 || device >= 64) return fail(CP_ATTN_ERR_INVALID_ARG, "device index out of range");
+  if (!buf[device]) {
+    cp_attn_status rc = hip_check(hipHostMalloc((void**)&buf[device], SW_COUNT * sizeof(int32_t), hipHostMallocDefault),
+                                  "hipHostMalloc(summary)");
+    if (rc != CP_ATTN_OK) {
+      buf[device] = nullptr;
+      return rc;
+    }
+  }
+  *out = buf[device];
+  return CP_ATTN_OK;
+}
+
 extern "C" {
 
 const char* cp_attn_last_error(void) { return g_last_error.c_str(); }
@@ -416,16 +438,12 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
   m->t_alloc = t_alloc;
   m->lay = make_layout(B, cp_size, t_alloc);
   m->d_tab = nullptr;
-  m->h_summary = nullptr;
   cp_attn_status rc;
+  int32_t* h_sum = nullptr;
   if ((rc = hip_check(hipGetDevice(&m->device), "hipGetDevice")) != CP_ATTN_OK) { delete m; return rc; }
+  if ((rc = summary_buffer(m->device, &h_sum)) != CP_ATTN_OK) { delete m; return rc; }
   if ((rc = hip_check(hipMalloc(&m->d_tab, m->lay.total * sizeof(int32_t)), "hipMalloc(meta)")) != CP_ATTN_OK) {
     delete m;
-    return rc;
-  }
-  if ((rc = hip_check(hipHostMalloc((void**)&m->h_summary, SW_COUNT * sizeof(int32_t), hipHostMallocDefault),
-                      "hipHostMalloc(summary)")) != CP_ATTN_OK) {
-    cp_attn_meta_free(m);
     return rc;
   }
   const MetaLayout& L = m->lay;
@@ -444,7 +462,7 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
   }
   hipLaunchKernelGGL(meta_sort_kernel, dim3(2 * cp_size), dim3(1024), 0, st, m->d_tab, L, B, cp_size);
   if ((rc = hip_check(hipGetLastError(), "metadata kernel launch")) != CP_ATTN_OK) { cp_attn_meta_free(m); return rc; }
-  if ((rc = hip_check(hipMemcpyAsync(m->h_summary, m->d_tab + L.summary, SW_COUNT * sizeof(int32_t),
+  if ((rc = hip_check(hipMemcpyAsync(h_sum, m->d_tab + L.summary, SW_COUNT * sizeof(int32_t),
                                      hipMemcpyDeviceToHost, st),
                       "hipMemcpyAsync(summary)")) != CP_ATTN_OK) {
     cp_attn_meta_free(m);
@@ -454,7 +472,7 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
     cp_attn_meta_free(m);
     return rc;
   }
-  const int32_t* sw = m->h_summary;
+  const int32_t* sw = h_sum;
   int err = sw[SW_ERR];
   if (err) {
     cp_attn_status code = (err == ME_HINT) ? CP_ATTN_ERR_HINT_MISMATCH : CP_ATTN_ERR_INVALID_ARG;
@@ -534,7 +552,6 @@ void cp_attn_meta_free(cp_attn_meta* m) {
     hipDeviceSynchronize();
     hipFree(m->d_tab);
   }
-  if (m->h_summary) hipHostFree(m->h_summary);
   if (cur != m->device) hipSetDevice(cur);
   delete m;
 }

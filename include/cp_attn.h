@@ -82,8 +82,10 @@ typedef struct {
 
 /*
  * Build rank cp_rank's per-batch metadata on the device (one small kernel
- * group, then ONE host synchronisation to read back a <1 KB summary; the only
- * synchronisation in the library). [I2] "Describe the bug": the per-step
+ * group, then ONE host synchronisation of `stream` to read back a <1 KB
+ * summary; the only synchronisation in the library). The summary lands in a
+ * pinned host buffer that each calling thread keeps per device until the
+ * process ends. [I2] "Describe the bug": the per-step
  * per-rank cu_seqlens; [I2] "Expected behavior": the padding decision is
  * taken from values only - the library never compares pointers, so an
  * aliased, NULL or distinct-but-equal cu_seqlens_padded all yield identical
