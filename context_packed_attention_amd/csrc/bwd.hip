@@ -512,33 +512,45 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
       }
     }
   }
-  // write this lane's key rows: d = 32 md + 8 (j / 4) + 4 g + (j % 4)
+  // The block's key rows leave through LDS (the Q, dO and V tiles are free
+  // now): each lane parks its rows' dK / dV values (d = 32 md + 8 (j / 4) +
+  // 4 g + (j % 4)) in padded row-major staging tiles, then every global
+  // store writes 16 bytes of a whole row, 16 lanes per row of D = 128.
+  constexpr int SP = D * 2 + 16;  // staging row pitch in bytes
+  static_assert(BK * SP <= (int)sizeof(Vt), "dK staging fits the V tile");
+  static_assert((BK / 2) * SP <= (int)sizeof(Qs) && (BK / 2) * SP <= (int)sizeof(Ds), "dV staging fits Q and dO");
+  char* const stk = reinterpret_cast<char*>(Vt);
+  auto stv = [&](int r) {
+    return r < BK / 2 ? reinterpret_cast<char*>(&Qs[0][0]) + r * SP : reinterpret_cast<char*>(&Ds[0][0]) + (r - BK / 2) * SP;
+  };
+  __syncthreads();  // every wavefront is done with the Q, dO and V tiles
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int r = wr0 + kb * 32 + l32;
-    if (r < rows_here) {
-      const int key = k0 + r;
-      const bool ok = key < kl;
-      uint16_t* dkr = sts.dk[si] + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
-      uint16_t* dvr = sts.dv[si] + (long long)(kvs + key) * p.ld_kv + kvh * D + g * 4;
+    const bool ok = k0 + r < kl;  // key rows past the step's key range are written as zeros
 #pragma unroll
-      for (int md = 0; md < NMD; ++md)
+    for (int md = 0; md < NMD; ++md)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          uint2 a, b;
-          if (ok) {
-            a.x = pack2_bf16(dk[kb][md][4 * jj] * p.scale, dk[kb][md][4 * jj + 1] * p.scale);
-            a.y = pack2_bf16(dk[kb][md][4 * jj + 2] * p.scale, dk[kb][md][4 * jj + 3] * p.scale);
-            b.x = pack2_bf16(dv[kb][md][4 * jj], dv[kb][md][4 * jj + 1]);
-            b.y = pack2_bf16(dv[kb][md][4 * jj + 2], dv[kb][md][4 * jj + 3]);
-          } else {
-            a = make_uint2(0, 0);
-            b = make_uint2(0, 0);
-          }
-          *reinterpret_cast<uint2*>(dkr + md * 32 + jj * 8) = a;
-          *reinterpret_cast<uint2*>(dvr + md * 32 + jj * 8) = b;
+      for (int jj = 0; jj < 4; ++jj) {
+        uint2 a = make_uint2(0, 0), b = make_uint2(0, 0);
+        if (ok) {
+          a.x = pack2_bf16(dk[kb][md][4 * jj] * p.scale, dk[kb][md][4 * jj + 1] * p.scale);
+          a.y = pack2_bf16(dk[kb][md][4 * jj + 2] * p.scale, dk[kb][md][4 * jj + 3] * p.scale);
+          b.x = pack2_bf16(dv[kb][md][4 * jj], dv[kb][md][4 * jj + 1]);
+          b.y = pack2_bf16(dv[kb][md][4 * jj + 2], dv[kb][md][4 * jj + 3]);
         }
-    }
+        const int cb = (md * 32 + jj * 8 + g * 4) * 2;
+        *reinterpret_cast<uint2*>(stk + r * SP + cb) = a;
+        *reinterpret_cast<uint2*>(stv(r) + cb) = b;
+      }
+  }
+  __syncthreads();
+  constexpr int UPR = D * 2 / 16;  // 16-byte units per row
+  for (int u = tid; u < rows_here * UPR; u += BLOCK_THREADS) {
+    const int r = u / UPR, c = u - r * UPR;
+    const long long e = (long long)(kvs + k0 + r) * p.ld_kv + kvh * D + c * 8;
+    *reinterpret_cast<uint4*>(sts.dk[si] + e) = *reinterpret_cast<const uint4*>(stk + r * SP + c * 16);
+    *reinterpret_cast<uint4*>(sts.dv[si] + e) = *reinterpret_cast<const uint4*>(stv(r) + c * 16);
   }
 }
 
