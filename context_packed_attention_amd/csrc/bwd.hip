@@ -255,18 +255,14 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
     cur = nxt;
     ++it;
   }
-  if (qok) {
-    uint16_t* dst = p.dq + (long long)(base + qrow) * p.hq * D + head * D + g * 4;
-#pragma unroll
-    for (int md = 0; md < NMD; ++md)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        uint2 pk;
-        pk.x = pack2_bf16(acc[md][4 * jj] * p.scale, acc[md][4 * jj + 1] * p.scale);
-        pk.y = pack2_bf16(acc[md][4 * jj + 2] * p.scale, acc[md][4 * jj + 3] * p.scale);
-        *reinterpret_cast<uint2*>(dst + md * 32 + jj * 8) = pk;
-      }
-  }
+  // bf16 dQ through LDS (the K tiles are free), whole-row stores
+  constexpr int SP = D * 2 + 16;
+  static_assert(BM * SP <= (int)sizeof(Ks), "dQ staging fits the K tiles");
+  char* const stage = reinterpret_cast<char*>(&Ks[0][0]);
+  __syncthreads();  // every wavefront is done with the K and V tiles
+  stage_row_bf16<D>(stage + (w * 32 + l32) * SP, g, acc, p.scale);
+  __syncthreads();
+  store_rows<D, SP, BLOCK_THREADS>(stage, nq, p.dq + (long long)(base + q0) * p.hq * D + head * D, (long long)p.hq * D, tid);
 }
 
 // dK/dV of one ring step for the source shard's key rows. Block = NWAVES

@@ -289,6 +289,20 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   }
 
   const float lt = sum_halves(l_run);
+  if constexpr (FUSED) {
+    // every step is in: the bf16 output (through LDS, whole-row stores; the
+    // K tiles are free) and the final LSE
+    constexpr int SP = D * 2 + 16;
+    static_assert(FWD_BM * SP <= (int)sizeof(Ks), "output staging fits the K tiles");
+    char* const stage = reinterpret_cast<char*>(&Ks[0][0]);
+    __syncthreads();  // every wavefront is done with the K and V tiles
+    stage_row_bf16<D>(stage + (w * 32 + l32) * SP, g, o, lt > 0.f ? 1.f / lt : 0.f);
+    if (qrow < ql && g == 0)
+      p.lse_out[(long long)head * p.ld_lse_out + qs + qrow] = lt > 0.f ? m_run * p.scale + __logf(lt) : NEG_INF_F;
+    __syncthreads();
+    store_rows<D, SP, BLOCK_THREADS>(stage, nq, p.out + (long long)(qs + q0) * p.ld_o + head * D, p.ld_o, tid);
+    return;
+  }
   if (qrow < ql) {
     float inv, lse;
     if (lt > 0.f) {
@@ -299,21 +313,6 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       lse = NEG_INF_F;
     }
     const int t = qs + qrow;  // local row
-    if constexpr (FUSED) {
-      // every step is in: the bf16 output and the final LSE
-      uint16_t* out_row = p.out + (long long)t * p.ld_o + head * D + g * 4;
-#pragma unroll
-      for (int md = 0; md < NMD; ++md)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          uint2 pk;
-          pk.x = pack2_bf16(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv);
-          pk.y = pack2_bf16(o[md][4 * jj + 2] * inv, o[md][4 * jj + 3] * inv);
-          *reinterpret_cast<uint2*>(out_row + md * 32 + jj * 8) = pk;
-        }
-      if (g == 0) p.lse_out[(long long)head * p.ld_lse_out + t] = lse;
-      return;
-    }
     float* orow = st.o[si] + (long long)t * p.ld_o + head * D + g * 4;
     float* lrow = st.lse[si] + (long long)head * p.ld_lse + t;
     if (p.mode == 0) {

@@ -99,6 +99,35 @@ __device__ __forceinline__ void store_transposed_4x8(uint16_t* dst, int stride, 
   }
 }
 
+// Output rows through LDS. In the MFMA accumulator layout a lane holds
+// elements d = 32 md + 8 jj + 4 g + e (e = 0..3) of one row; parking them in
+// a padded row-major staging tile lets every global store write 16 bytes of
+// a whole row (D * 2 / 16 lanes per row) instead of 8 bytes in each of 32
+// rows. stage_row_bf16 writes one lane's share of `row` (scaled by mul);
+// store_rows copies staging rows [0, n) to dst rows (ld elements apart)
+// with every thread of the block.
+template <int D>
+__device__ __forceinline__ void stage_row_bf16(char* row, int g, const f32x16_t (&v)[D / 32], float mul) {
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint2 pk;
+      pk.x = pack2_bf16(v[md][4 * jj] * mul, v[md][4 * jj + 1] * mul);
+      pk.y = pack2_bf16(v[md][4 * jj + 2] * mul, v[md][4 * jj + 3] * mul);
+      *reinterpret_cast<uint2*>(row + (md * 32 + jj * 8 + g * 4) * 2) = pk;
+    }
+}
+
+template <int D, int PITCH, int THREADS>
+__device__ __forceinline__ void store_rows(const char* stage, int n, uint16_t* dst, long long ld, int tid) {
+  constexpr int UPR = D * 2 / 16;
+  for (int u = tid; u < n * UPR; u += THREADS) {
+    const int r = u / UPR, c = u - r * UPR;
+    *reinterpret_cast<uint4*>(dst + (long long)r * ld + c * 8) = *reinterpret_cast<const uint4*>(stage + r * PITCH + c * 16);
+  }
+}
+
 // Block -> (work item, head). When the head count is a multiple of the 8
 // XCDs, the blocks that land on one XCD (consecutive ids are dealt to the
 // XCDs round-robin) take a contiguous run of heads, so a GQA group's K/V stay
