@@ -675,8 +675,22 @@ def main():
         meta_ms.append((time.perf_counter() - t) * 1e3)
         m.close()
 
-    def one_step():
-        m = api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+    # A step = this batch's metadata, forward and backward. The metadata comes
+    # from the host copies of cu_seqlens (the batch's lengths are on the host,
+    # where a data loader makes them) through the path that needs no host
+    # synchronisation; packs of more sequences than it carries use the device
+    # path. The device path's step time is reported beside it.
+    cu_h = np.asarray(batch.cu, dtype=np.int32)
+    cup_h = np.asarray(batch.cup, dtype=np.int32)
+    host_meta = len(cu_h) - 1 <= 255
+
+    def make_meta(host):
+        if host:
+            return api.cp_attn_rank_metadata_host(cu_h, cup_h, cp, rank, -1, t_alloc, stream=stream)
+        return api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+
+    def one_step(host=host_meta):
+        m = make_meta(host)
         api.cp_attn_fwd(m, q, ks, vs, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream)
         api.cp_attn_bwd(m, q, ks, vs, out, lse, do, hq, hkv, d, scale, 1, dq, dks, dvs, ws_b, stream=stream)
         return m
@@ -685,20 +699,45 @@ def main():
     held = []
     for _ in range(args.warmup):
         held.append(one_step())
+    # the timed passes hold every step's handle until they end; the library
+    # pools the handles' device buffers, so K of them are built and freed
+    # here first (untimed), as a training loop's first steps would
+    held += [make_meta(host_meta) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for m in held:
         m.close()
     held.clear()
-    log(f"[bench] timing {args.steps} steps")
+    # per-kernel times: the same K steps with an event pair around every
+    # launch (kept out of the timed pass: on short packs the events cost
+    # several percent of a step)
     api.cp_attn_timing_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        held.append(one_step())
+    torch.cuda.synchronize()
+    api.cp_attn_timing_enable(False)
+    per_kernel = api.cp_attn_timing_read()
+    for m in held:
+        m.close()
+    held.clear()
+    # the same steps with the device metadata path (one host wait per step)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        held.append(one_step(False))
+    torch.cuda.synchronize()
+    device_meta_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    for m in held:
+        m.close()
+    held.clear()
+    # the timed pass, last: the two passes above keep the GPU busy before it
+    log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         held.append(one_step())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    api.cp_attn_timing_enable(False)
-    per_kernel = api.cp_attn_timing_read()
     for m in held:
         m.close()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -730,7 +769,9 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(dom, w["name"]),
-                "algo_flops_per_launch": per_launch, "avg_launch_ms": dom_ms / dom_n}
+                "algo_flops_per_launch": per_launch, "avg_launch_ms": dom_ms / dom_n,
+                "timing": "HIP event pair around every launch on its own stream, over a second pass of the "
+                          "same timed steps"}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None}
@@ -802,6 +843,9 @@ def main():
                    "pairs": pairs, "step_pairs": step_pairs, "flops_per_step": flops_step, "t_alloc": t_alloc,
                    "parallelism": "one CP rank's share, all ring steps on one GPU"},
         "metadata_call_ms": round(sorted(meta_ms)[len(meta_ms) // 2], 4),
+        "metadata": ("host copies of cu_seqlens, no host synchronisation" if host_meta else "device path") +
+                    "; built every step inside the timed region",
+        "ms_per_step_device_metadata": round(device_meta_ms, 4),
         "kernels": kernels,
         "roofline": roof,
         "graph": graph_info,

@@ -19,7 +19,7 @@ ERR_HIP = 5
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "HINT_MISMATCH", 4: "WORKSPACE", 5: "HIP"}
 
 EXPORTED = [
-    "cp_attn_rank_metadata", "cp_attn_meta_summary", "cp_attn_meta_export", "cp_attn_meta_free",
+    "cp_attn_rank_metadata", "cp_attn_rank_metadata_host", "cp_attn_meta_summary", "cp_attn_meta_export", "cp_attn_meta_free",
     "cp_attn_workspace_bytes", "cp_attn_fwd", "cp_attn_bwd", "cp_attn_bwd_noalloc", "cp_attn_shard_gather", "cp_attn_last_error",
     "cp_attn_timing_enable", "cp_attn_timing_read",
     "cp_attn_graph_capture", "cp_attn_graph_launch", "cp_attn_graph_kernels", "cp_attn_graph_free",
@@ -56,6 +56,8 @@ def load(path: str | None = None) -> C.CDLL:
     st = C.c_int
     lib.cp_attn_rank_metadata.argtypes = [vp, vp, i32, i32, i32, i32, C.c_int64, vp, C.POINTER(vp)]
     lib.cp_attn_rank_metadata.restype = st
+    lib.cp_attn_rank_metadata_host.argtypes = [vp, vp, i32, i32, i32, i32, C.c_int64, vp, C.POINTER(vp)]
+    lib.cp_attn_rank_metadata_host.restype = st
     lib.cp_attn_meta_summary.argtypes = [vp, C.POINTER(Summary)]
     lib.cp_attn_meta_summary.restype = st
     lib.cp_attn_meta_export.argtypes = [vp, C.POINTER(C.c_int32), C.c_size_t, C.POINTER(C.c_size_t)]

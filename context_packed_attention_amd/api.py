@@ -137,6 +137,25 @@ def cp_attn_rank_metadata(cu_seqlens, cu_seqlens_padded, cp_size: int, cp_rank: 
     return Meta(h.value, int(t_alloc))
 
 
+def cp_attn_rank_metadata_host(cu_seqlens, cu_seqlens_padded, cp_size: int, cp_rank: int, pad_hint: int = -1,
+                               t_alloc: int | None = None, stream=None) -> Meta:
+    """The same handle from HOST int32 sequences [B+1] (numpy arrays or lists;
+    padded may be None), with no synchronisation."""
+    if t_alloc is None:
+        raise ValueError("t_alloc is required")
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    cup = None if cu_seqlens_padded is None else np.ascontiguousarray(cu_seqlens_padded, dtype=np.int32)
+    if cu.ndim != 1 or cu.size < 2 or (cup is not None and cup.shape != cu.shape):
+        raise ValueError("cu_seqlens / cu_seqlens_padded must be 1-D of the same length >= 2")
+    h = C.c_void_p()
+    rc = L.load().cp_attn_rank_metadata_host(cu.ctypes.data_as(C.c_void_p),
+                                             None if cup is None else cup.ctypes.data_as(C.c_void_p),
+                                             int(cu.size - 1), int(cp_size), int(cp_rank), int(pad_hint),
+                                             int(t_alloc), _stream(stream), C.byref(h))
+    _check(rc, "cp_attn_rank_metadata_host")
+    return Meta(h.value, int(t_alloc))
+
+
 def cp_attn_meta_export(meta: Meta) -> np.ndarray:
     lib = L.load()
     n = C.c_size_t()

@@ -82,7 +82,8 @@ struct cp_attn_meta {
   int B, cp, rank, pad_hint;
   int64_t t_alloc;
   cpattn::MetaLayout lay;
-  int32_t* d_tab;  // device tables
+  int32_t* d_tab;    // device tables
+  size_t tab_bytes;  // size of the d_tab buffer (from the per-device pool)
   cp_attn_summary sum;
 };
 

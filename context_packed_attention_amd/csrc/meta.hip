@@ -12,7 +12,9 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -97,12 +99,28 @@ __device__ int block_excl_scan256(int v, int* sm, int* total) {
   return before + x - v;
 }
 
+// Where the tables kernel reads cu_seqlens / cu_seqlens_padded: device
+// arrays (cup NULL = no padding), or the values themselves carried in the
+// kernel's arguments (the host path, B <= CP_ATTN_HOST_META_MAX_B).
+struct DevSeqlens {
+  const int32_t* cu;
+  const int32_t* cup;
+  __device__ int a(int b) const { return cu[b]; }
+  __device__ int p(int b) const { return cup ? cup[b] : cu[b]; }
+};
+struct ArgSeqlens {
+  int32_t cu[CP_ATTN_HOST_META_MAX_B + 1];
+  int32_t cup[CP_ATTN_HOST_META_MAX_B + 1];
+  __device__ int a(int b) const { return cu[b]; }
+  __device__ int p(int b) const { return cup[b]; }
+};
+
 // One block of 256 threads. Builds every per-sequence table, the validation
 // word, the padding decision and the per-step work-item offsets.
-__global__ void __launch_bounds__(256) meta_tables_kernel(const int32_t* __restrict__ cu_in,
-                                                          const int32_t* __restrict__ cup_in, int B, int cp,
-                                                          int rank, int hint, long long t_alloc,
-                                                          int32_t* __restrict__ tabp, MetaLayout L) {
+template <class Src>
+__global__ void __launch_bounds__(256) meta_tables_kernel(Src src, int B, int cp, int rank, int hint,
+                                                          long long t_alloc, int32_t* __restrict__ tabp,
+                                                          MetaLayout L) {
   __shared__ int sm[256];
   __shared__ int s_err, s_pad;
   __shared__ int s_carry[5 * CP_ATTN_MAX_CP];
@@ -113,12 +131,11 @@ __global__ void __launch_bounds__(256) meta_tables_kernel(const int32_t* __restr
   }
   if (t < 5 * CP_ATTN_MAX_CP) s_carry[t] = 0;
   __syncthreads();
-  const int32_t* cup_src = cup_in ? cup_in : cu_in;
   int32_t* cu = tabp + L.cu;
   int32_t* cup = tabp + L.cup;
   // copy inputs + elementwise checks
   for (int b = t; b <= B; b += 256) {
-    int a = cu_in[b], p = cup_src[b];
+    const int a = src.a(b), p = src.p(b);
     cu[b] = a;
     cup[b] = p;
     if (a != p) atomicOr(&s_pad, 1);
@@ -412,23 +429,71 @@ static cp_attn_status summary_buffer(int device, int32_t** out) {
   return CP_ATTN_OK;
 }
 
-extern "C" {
+// Device table buffers. A freed handle's buffer (the free synchronises the
+// device first, so no queued kernel still reads it) goes back to a free list
+// of its device, and the next handle on that device whose tables fit takes
+// it: steady-state metadata builds call no hipMalloc. At most POOL_MAX
+// buffers per device are kept, until the process ends.
+namespace {
+constexpr size_t POOL_MAX = 64;
+struct TabPool {
+  std::mutex mu;
+  std::vector<std::pair<int32_t*, size_t>> free;
+};
+TabPool g_pool[64];
+}  // namespace
 
-const char* cp_attn_last_error(void) { return g_last_error.c_str(); }
+static cp_attn_status tab_alloc(int device, size_t bytes, int32_t** p, size_t* got) {
+  bytes = (bytes + 65535) & ~size_t(65535);
+  if (device >= 0 && device < 64) {
+    TabPool& tp = g_pool[device];
+    std::lock_guard<std::mutex> lk(tp.mu);
+    int best = -1;
+    for (int i = 0; i < (int)tp.free.size(); ++i)
+      if (tp.free[i].second >= bytes && tp.free[i].second <= 4 * bytes &&
+          (best < 0 || tp.free[i].second < tp.free[best].second))
+        best = i;
+    if (best >= 0) {
+      *p = tp.free[best].first;
+      *got = tp.free[best].second;
+      tp.free.erase(tp.free.begin() + best);
+      return CP_ATTN_OK;
+    }
+  }
+  *got = bytes;
+  return hip_check(hipMalloc(p, bytes), "hipMalloc(meta)");
+}
 
-cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t B,
-                                     int32_t cp_size, int32_t cp_rank, int32_t pad_hint, int64_t t_alloc,
-                                     void* stream, cp_attn_meta** out) {
-  set_error("");
+static void tab_release(int device, int32_t* p, size_t bytes) {
+  if (device >= 0 && device < 64) {
+    TabPool& tp = g_pool[device];
+    std::lock_guard<std::mutex> lk(tp.mu);
+    if (tp.free.size() < POOL_MAX) {
+      tp.free.emplace_back(p, bytes);
+      return;
+    }
+  }
+  hipFree(p);
+}
+
+static cp_attn_status check_meta_args(const int32_t* cu, int B, int cp_size, int cp_rank, int pad_hint,
+                                      int64_t t_alloc, cp_attn_meta** out) {
   if (!out) return fail(CP_ATTN_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  if (!cu_seqlens) return fail(CP_ATTN_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (!cu) return fail(CP_ATTN_ERR_INVALID_ARG, "cu_seqlens is NULL");
   if (B < 1) return fail(CP_ATTN_ERR_INVALID_ARG, "B must be >= 1");
   if (cp_size < 1 || cp_size > CP_ATTN_MAX_CP) return fail(CP_ATTN_ERR_UNSUPPORTED, "cp_size must be in [1, 16]");
   if (cp_rank < 0 || cp_rank >= cp_size) return fail(CP_ATTN_ERR_INVALID_ARG, "cp_rank out of range");
   if (pad_hint < -1 || pad_hint > 1) return fail(CP_ATTN_ERR_INVALID_ARG, "pad_hint must be -1, 0 or 1");
   if (t_alloc < 0 || t_alloc >= (1ll << 30)) return fail(CP_ATTN_ERR_INVALID_ARG, "t_alloc out of range");
-  hipStream_t st = (hipStream_t)stream;
+  return CP_ATTN_OK;
+}
+
+// A handle with its device tables, and the metadata kernels launched on st
+// (the tables kernel reading its inputs from src).
+template <class Src>
+static cp_attn_status launch_meta(const Src& src, int B, int cp_size, int cp_rank, int pad_hint, int64_t t_alloc,
+                                  hipStream_t st, cp_attn_meta** out) {
   cp_attn_meta* m = new cp_attn_meta();
   std::memset(&m->sum, 0, sizeof(m->sum));
   m->B = B;
@@ -438,17 +503,20 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
   m->t_alloc = t_alloc;
   m->lay = make_layout(B, cp_size, t_alloc);
   m->d_tab = nullptr;
+  m->sum.B = B;
+  m->sum.cp_size = cp_size;
+  m->sum.cp_rank = cp_rank;
+  m->sum.t_alloc = t_alloc;
   cp_attn_status rc;
-  int32_t* h_sum = nullptr;
   if ((rc = hip_check(hipGetDevice(&m->device), "hipGetDevice")) != CP_ATTN_OK) { delete m; return rc; }
-  if ((rc = summary_buffer(m->device, &h_sum)) != CP_ATTN_OK) { delete m; return rc; }
-  if ((rc = hip_check(hipMalloc(&m->d_tab, m->lay.total * sizeof(int32_t)), "hipMalloc(meta)")) != CP_ATTN_OK) {
+  m->tab_bytes = 0;
+  if ((rc = tab_alloc(m->device, m->lay.total * sizeof(int32_t), &m->d_tab, &m->tab_bytes)) != CP_ATTN_OK) {
     delete m;
     return rc;
   }
   const MetaLayout& L = m->lay;
-  hipLaunchKernelGGL(meta_tables_kernel, dim3(1), dim3(256), 0, st, cu_seqlens, cu_seqlens_padded, B, cp_size,
-                     cp_rank, pad_hint, (long long)t_alloc, m->d_tab, L);
+  hipLaunchKernelGGL(meta_tables_kernel<Src>, dim3(1), dim3(256), 0, st, src, B, cp_size, cp_rank, pad_hint,
+                     (long long)t_alloc, m->d_tab, L);
   {
     long long blocks = std::min<long long>((t_alloc + 255) / 256, 4096);
     if (blocks < 1) blocks = 1;
@@ -461,7 +529,80 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
     hipLaunchKernelGGL(meta_tiles_kernel, dim3(bx, 2 * cp_size), dim3(256), 0, st, m->d_tab, L, B, cp_size);
   }
   hipLaunchKernelGGL(meta_sort_kernel, dim3(2 * cp_size), dim3(1024), 0, st, m->d_tab, L, B, cp_size);
-  if ((rc = hip_check(hipGetLastError(), "metadata kernel launch")) != CP_ATTN_OK) { cp_attn_meta_free(m); return rc; }
+  if ((rc = hip_check(hipGetLastError(), "metadata kernel launch")) != CP_ATTN_OK) {
+    cp_attn_meta_free(m);
+    return rc;
+  }
+  *out = m;
+  return CP_ATTN_OK;
+}
+
+// The summary and the validation word from host copies of the inputs: the
+// same arithmetic as the tables kernel's (chunk sizes P_b / (2 CP), valid
+// rows per chunk, step kinds and sources, work-item counts per step).
+static int host_summary(const int32_t* cu, const int32_t* cup_in, int B, int cp, int rank, int hint, int64_t t_alloc,
+                        cp_attn_summary* s) {
+  const int32_t* cup = cup_in ? cup_in : cu;
+  auto cv = [](int L, int c, int k) { return std::min(std::max(L - k * c, 0), c); };
+  const int two_cp = 2 * cp;
+  int err = 0, pad = 0;
+  if (cu[0] != 0 || cup[0] != 0) err |= ME_START;
+  for (int b = 0; b <= B; ++b)
+    if (cu[b] != cup[b]) pad = 1;
+  for (int i = 0; i < cp; ++i) {
+    const int src = ((rank - i) % cp + cp) % cp;
+    s->step_src[i] = src;
+    s->step_kind[i] = i == 0 ? 0 : (src < rank ? 1 : 2);
+  }
+  int64_t valid = 0;
+  for (int b = 0; b < B; ++b) {
+    int Lb = cu[b + 1] - cu[b], Pb = cup[b + 1] - cup[b];
+    if (Lb < 0) err |= ME_CU_ORDER;
+    if (Pb < 0) err |= ME_CUP_ORDER;
+    if (Lb > Pb) err |= ME_LEN;
+    if (Pb >= 0 && Pb % two_cp != 0) err |= ME_DIV;
+    if (Pb < 0) Pb = 0;
+    Lb = std::min(std::max(Lb, 0), Pb);
+    const int c = Pb / two_cp;
+    const int fr = cv(Lb, c, rank), sr = cv(Lb, c, two_cp - 1 - rank);
+    valid += fr + sr;
+    for (int i = 0; i < cp; ++i) {
+      const int q_len = s->step_kind[i] == 2 ? sr : fr + sr;
+      s->tiles_fwd[i] += (q_len + FWD_BM - 1) / FWD_BM;
+      s->tiles_dkdv[i] += (Pb / cp + DKDV_BN - 1) / DKDV_BN;
+    }
+  }
+  const int64_t tl = (int64_t)cup[B] / cp;
+  if (tl > t_alloc) err |= ME_ALLOC;
+  if (tl >= (1ll << 30)) err |= ME_RANGE;
+  if (hint >= 0 && hint != pad) err |= ME_HINT;
+  s->pad_between_seqs = pad;
+  s->t_local = (int32_t)tl;
+  s->has_tail = t_alloc > tl ? 1 : 0;
+  s->valid_rows = valid;
+  return err;
+}
+
+extern "C" {
+
+const char* cp_attn_last_error(void) { return g_last_error.c_str(); }
+
+cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t B,
+                                     int32_t cp_size, int32_t cp_rank, int32_t pad_hint, int64_t t_alloc,
+                                     void* stream, cp_attn_meta** out) {
+  set_error("");
+  cp_attn_status rc = check_meta_args(cu_seqlens, B, cp_size, cp_rank, pad_hint, t_alloc, out);
+  if (rc != CP_ATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* h_sum = nullptr;
+  int device = 0;
+  if ((rc = hip_check(hipGetDevice(&device), "hipGetDevice")) != CP_ATTN_OK) return rc;
+  if ((rc = summary_buffer(device, &h_sum)) != CP_ATTN_OK) return rc;
+  cp_attn_meta* m = nullptr;
+  if ((rc = launch_meta(DevSeqlens{cu_seqlens, cu_seqlens_padded}, B, cp_size, cp_rank, pad_hint, t_alloc, st, &m)) !=
+      CP_ATTN_OK)
+    return rc;
+  const MetaLayout& L = m->lay;
   if ((rc = hip_check(hipMemcpyAsync(h_sum, m->d_tab + L.summary, SW_COUNT * sizeof(int32_t),
                                      hipMemcpyDeviceToHost, st),
                       "hipMemcpyAsync(summary)")) != CP_ATTN_OK) {
@@ -473,21 +614,15 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
     return rc;
   }
   const int32_t* sw = h_sum;
-  int err = sw[SW_ERR];
+  const int err = sw[SW_ERR];
   if (err) {
-    cp_attn_status code = (err == ME_HINT) ? CP_ATTN_ERR_HINT_MISMATCH : CP_ATTN_ERR_INVALID_ARG;
-    std::string msg = describe_meta_error(err);
     cp_attn_meta_free(m);
-    return fail(code, msg);
+    return fail(err == ME_HINT ? CP_ATTN_ERR_HINT_MISMATCH : CP_ATTN_ERR_INVALID_ARG, describe_meta_error(err));
   }
   cp_attn_summary& s = m->sum;
-  s.B = B;
-  s.cp_size = cp_size;
-  s.cp_rank = cp_rank;
   s.pad_between_seqs = sw[SW_PAD];
   s.t_local = sw[SW_TLOCAL];
   s.has_tail = sw[SW_HAS_TAIL];
-  s.t_alloc = t_alloc;
   s.valid_rows = sw[SW_VALID_ROWS];
   for (int i = 0; i < cp_size; ++i) {
     s.step_kind[i] = sw[SW_KIND + i];
@@ -495,6 +630,35 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
     s.tiles_fwd[i] = sw[SW_TILES_FWD + i];
     s.tiles_dkdv[i] = sw[SW_TILES_DKDV + i];
   }
+  *out = m;
+  return CP_ATTN_OK;
+}
+
+cp_attn_status cp_attn_rank_metadata_host(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t B,
+                                          int32_t cp_size, int32_t cp_rank, int32_t pad_hint, int64_t t_alloc,
+                                          void* stream, cp_attn_meta** out) {
+  set_error("");
+  cp_attn_status rc = check_meta_args(cu_seqlens, B, cp_size, cp_rank, pad_hint, t_alloc, out);
+  if (rc != CP_ATTN_OK) return rc;
+  if (B > CP_ATTN_HOST_META_MAX_B)
+    return fail(CP_ATTN_ERR_UNSUPPORTED, "more sequences than the host path carries; use cp_attn_rank_metadata");
+  cp_attn_summary s{};
+  const int err = host_summary(cu_seqlens, cu_seqlens_padded, B, cp_size, cp_rank, pad_hint, t_alloc, &s);
+  if (err) return fail(err == ME_HINT ? CP_ATTN_ERR_HINT_MISMATCH : CP_ATTN_ERR_INVALID_ARG, describe_meta_error(err));
+  ArgSeqlens vals;
+  for (int b = 0; b <= B; ++b) {
+    vals.cu[b] = cu_seqlens[b];
+    vals.cup[b] = cu_seqlens_padded ? cu_seqlens_padded[b] : cu_seqlens[b];
+  }
+  cp_attn_meta* m = nullptr;
+  if ((rc = launch_meta(vals, B, cp_size, cp_rank, pad_hint, t_alloc, (hipStream_t)stream, &m)) != CP_ATTN_OK)
+    return rc;
+  const cp_attn_summary keep = m->sum;  // B, ring and t_alloc, filled by launch_meta
+  m->sum = s;
+  m->sum.B = keep.B;
+  m->sum.cp_size = keep.cp_size;
+  m->sum.cp_rank = keep.cp_rank;
+  m->sum.t_alloc = keep.t_alloc;
   *out = m;
   return CP_ATTN_OK;
 }
@@ -550,7 +714,7 @@ void cp_attn_meta_free(cp_attn_meta* m) {
   if (cur != m->device) hipSetDevice(m->device);
   if (m->d_tab) {
     hipDeviceSynchronize();
-    hipFree(m->d_tab);
+    tab_release(m->device, m->d_tab, m->tab_bytes);
   }
   if (cur != m->device) hipSetDevice(cur);
   delete m;

@@ -58,6 +58,8 @@ typedef enum {
 } cp_attn_status;
 
 #define CP_ATTN_MAX_CP 16
+/* Most sequences per batch that cp_attn_rank_metadata_host accepts. */
+#define CP_ATTN_HOST_META_MAX_B 255
 
 /* Opaque per-batch metadata handle (device tables + host summary). */
 typedef struct cp_attn_meta cp_attn_meta;
@@ -109,6 +111,28 @@ cp_attn_status cp_attn_rank_metadata(const int32_t* cu_seqlens, const int32_t* c
                                      int32_t B, int32_t cp_size, int32_t cp_rank, int32_t pad_hint,
                                      int64_t t_alloc, void* stream, cp_attn_meta** out);
 
+/*
+ * cp_attn_rank_metadata from host copies of the same arrays, with no
+ * synchronisation: the summary and every validation check are computed on
+ * the host (the same arithmetic, so the same tables, summary, status and
+ * message), and the values travel to the device in the table kernel's launch
+ * arguments, so nothing the caller owns is read after the call returns. For
+ * a caller that holds the batch's cu_seqlens on the host (a data loader
+ * builds them there): the per-step host wait of the device path disappears
+ * and the next kernels queue straight behind the metadata kernels.
+ *
+ *  cu_seqlens, cu_seqlens_padded  HOST int32 [B+1] (padded: NULL = none);
+ *                     conditions and pad_hint as in cp_attn_rank_metadata
+ *  B                  1 .. CP_ATTN_HOST_META_MAX_B, else CP_ATTN_ERR_UNSUPPORTED
+ *  stream             the metadata kernels run on it; later calls with the
+ *                     handle must be ordered after them (same stream, or an
+ *                     event)
+ * Other arguments: as cp_attn_rank_metadata.
+ */
+cp_attn_status cp_attn_rank_metadata_host(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t B,
+                                          int32_t cp_size, int32_t cp_rank, int32_t pad_hint, int64_t t_alloc,
+                                          void* stream, cp_attn_meta** out);
+
 /* Copy the host summary (no device work). */
 cp_attn_status cp_attn_meta_summary(const cp_attn_meta* m, cp_attn_summary* out);
 
@@ -129,7 +153,10 @@ cp_attn_status cp_attn_meta_summary(const cp_attn_meta* m, cp_attn_summary* out)
  */
 cp_attn_status cp_attn_meta_export(const cp_attn_meta* m, int32_t* host_buf, size_t n, size_t* n_needed);
 
-/* Release the handle (synchronises the device it was built on). NULL is a no-op. */
+/* Release the handle (synchronises the device it was built on). Its device
+ * table buffer goes back to a per-device pool (at most 64 buffers, kept until
+ * the process ends) from which later handles take theirs, so steady-state
+ * metadata builds allocate nothing. NULL is a no-op. */
 void cp_attn_meta_free(cp_attn_meta* m);
 
 /* Workspace bytes needed by cp_attn_fwd (pass 0: one fp32 output accumulator

@@ -1,6 +1,8 @@
 """Device metadata builder vs the oracle: integer tables bit-exact, the padding
 decision taken from values (aliased / NULL / distinct-equal padded
-cu_seqlens all give identical tables), and device-side argument checks."""
+cu_seqlens all give identical tables), and device-side argument checks. The
+host-summary path (cp_attn_rank_metadata_host) must give the same tables,
+summary, statuses and messages, and the same forward / backward bits."""
 import numpy as np
 import pytest
 
@@ -58,7 +60,19 @@ def test_metadata_bit_exact(name, L, P, cp):
             s = m.summary
             assert s.has_tail == (1 if tail else 0)
             assert s.valid_rows == int(np.diff(ref[f"cu_full_{r}"]).sum())
+            mh = api.cp_attn_rank_metadata_host(cu, cup, cp, r, -1, T_local + tail)
+            assert np.array_equal(mh.export(), m.export())
+            assert _summary(mh) == _summary(m)
+            mh.close()
             m.close()
+
+
+def _summary(m):
+    s = m.summary
+    cp = int(s.cp_size)
+    return (int(s.B), cp, int(s.cp_rank), int(s.pad_between_seqs), int(s.t_local), int(s.has_tail), int(s.t_alloc),
+            int(s.valid_rows), list(s.step_kind)[:cp], list(s.step_src)[:cp], list(s.tiles_fwd)[:cp],
+            list(s.tiles_dkdv)[:cp])
 
 
 def test_padding_decision_by_value_not_identity():
@@ -100,6 +114,40 @@ def test_device_side_validation(cu, cup, hint, t_alloc, status):
     with pytest.raises(api.CpAttnError) as ei:
         api.cp_attn_rank_metadata(dcu, dcup, 4, 1, hint, t_alloc)
     assert ei.value.status == status
+    with pytest.raises(api.CpAttnError) as eh:
+        api.cp_attn_rank_metadata_host(cu, cup, 4, 1, hint, t_alloc)
+    assert eh.value.status == status and str(eh.value) == str(ei.value).replace(
+        "cp_attn_rank_metadata", "cp_attn_rank_metadata_host")
+
+
+@pytest.mark.parametrize("cfg,rank,tail", [(3, 1, 0), (1, 0, 37)])
+def test_host_path_same_results(cfg, rank, tail):
+    """Forward and backward with the host-path handle equal those with the
+    device-path handle bit for bit (the 16K padded pack; the tiny pack with a
+    tail)."""
+    import math
+    import torch
+    bt, w = synth.make_workload(cfg)
+    cp = w["cp"]
+    db = H.DeviceBatch(bt)
+    meta, loc = H.local_inputs(db, cp, rank, tail=tail)
+    scale = 1.0 / math.sqrt(bt.d)
+    res = []
+    for host in (False, True):
+        if host:
+            m = api.cp_attn_rank_metadata_host(bt.cu, bt.cup, cp, rank, -1, loc["t_alloc"])
+        else:
+            m = meta
+        out, lse = H.run_fwd(m, loc, bt, scale)
+        dq, dks, dvs = H.run_bwd(m, loc, bt, scale, out, lse)
+        torch.cuda.synchronize()
+        res.append([out, lse, dq, *dks, *dvs])
+        if host:
+            m.close()
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    meta.close()
 
 
 def test_shard_gather_matches_oracle_map():
