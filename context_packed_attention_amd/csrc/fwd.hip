@@ -61,6 +61,76 @@ struct FwdSteps {
   int n;
 };
 
+// A step's normalised partial for one lane's query row (local row t): mode 0
+// writes it, mode 1 folds it into the accumulator through the log-sum-exp,
+// mode 2 folds it and writes the bf16 output and the final LSE instead:
+//   out = (e^(la-m) out_a + e^(lb-m) out_b) / (e^(la-m) + e^(lb-m)),
+//   lse = m + log of that sum, m = max(la, lb).
+template <int D>
+__device__ __forceinline__ void step_epilogue(const FwdParams& p, float* o_part, float* l_part, int t, int head, int g,
+                                              const f32x16_t (&o)[D / 32], float m_run, float lt) {
+  constexpr int NMD = D / 32;
+  float inv, lse;
+  if (lt > 0.f) {
+    inv = 1.f / lt;
+    lse = m_run * p.scale + __logf(lt);
+  } else {
+    inv = 0.f;
+    lse = NEG_INF_F;
+  }
+  float* orow = o_part + (long long)t * p.ld_o + head * D + g * 4;
+  float* lrow = l_part + (long long)head * p.ld_lse + t;
+  if (p.mode == 0) {
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float4 val = make_float4(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
+                                 o[md][4 * jj + 3] * inv);
+        *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
+      }
+    if (g == 0) *lrow = lse;
+    return;
+  }
+  const bool has = (p.rowflags[t] & RF_SECOND) ? p.acc_second : p.acc_first;
+  const float la = has ? *lrow : NEG_INF_F;
+  const float mx = fmaxf(la, lse);
+  float wa = 0.f, wb = 0.f, lm = NEG_INF_F;
+  if (mx != NEG_INF_F) {
+    wa = __expf(la - mx);
+    wb = __expf(lse - mx);
+    const float ssum = wa + wb;
+    lm = mx + __logf(ssum);
+    const float r = 1.f / ssum;
+    wa *= r;
+    wb *= r * inv;
+  }
+  uint16_t* out_row = p.out + (long long)t * p.ld_o + head * D + g * 4;
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (has) a = *reinterpret_cast<const float4*>(orow + md * 32 + jj * 8);
+      const float4 val = make_float4(wa * a.x + wb * o[md][4 * jj], wa * a.y + wb * o[md][4 * jj + 1],
+                                     wa * a.z + wb * o[md][4 * jj + 2], wa * a.w + wb * o[md][4 * jj + 3]);
+      if (p.mode == 1) {
+        *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
+      } else {
+        uint2 pk;
+        pk.x = pack2_bf16(val.x, val.y);
+        pk.y = pack2_bf16(val.z, val.w);
+        *reinterpret_cast<uint2*>(out_row + md * 32 + jj * 8) = pk;
+      }
+    }
+  if (g == 0) {
+    if (p.mode == 1)
+      *lrow = lm;
+    else
+      p.lse_out[(long long)head * p.ld_lse_out + t] = lm;
+  }
+}
+
 // One block = NWAVES wavefronts (FWD_BM query rows) of one head; each wavefront owns
 // 32 query rows. K and V tiles of 64 rows are copied straight from global
 // memory into padded LDS tiles (buffer loads with the lds modifier, no
@@ -303,70 +373,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     store_rows<D, SP, BLOCK_THREADS>(stage, nq, p.out + (long long)(qs + q0) * p.ld_o + head * D, p.ld_o, tid);
     return;
   }
-  if (qrow < ql) {
-    float inv, lse;
-    if (lt > 0.f) {
-      inv = 1.f / lt;
-      lse = m_run * p.scale + __logf(lt);
-    } else {
-      inv = 0.f;
-      lse = NEG_INF_F;
-    }
-    const int t = qs + qrow;  // local row
-    float* orow = st.o[si] + (long long)t * p.ld_o + head * D + g * 4;
-    float* lrow = st.lse[si] + (long long)head * p.ld_lse + t;
-    if (p.mode == 0) {
-#pragma unroll
-      for (int md = 0; md < NMD; ++md)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float4 val = make_float4(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
-                                   o[md][4 * jj + 3] * inv);
-          *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
-        }
-      if (g == 0) *lrow = lse;
-    } else {
-      // fold into the accumulator: out = (e^(la-m) out_a + e^(lb-m) out_b) /
-      // (e^(la-m) + e^(lb-m)), lse = m + log of that sum, m = max(la, lb)
-      const bool has = (p.rowflags[t] & RF_SECOND) ? p.acc_second : p.acc_first;
-      const float la = has ? *lrow : NEG_INF_F;
-      const float mx = fmaxf(la, lse);
-      float wa = 0.f, wb = 0.f, lm = NEG_INF_F;
-      if (mx != NEG_INF_F) {
-        wa = __expf(la - mx);
-        wb = __expf(lse - mx);
-        const float ssum = wa + wb;
-        lm = mx + __logf(ssum);
-        const float r = 1.f / ssum;
-        wa *= r;
-        wb *= r * inv;
-      }
-      uint16_t* out_row = p.out + (long long)t * p.ld_o + head * D + g * 4;
-#pragma unroll
-      for (int md = 0; md < NMD; ++md)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (has) a = *reinterpret_cast<const float4*>(orow + md * 32 + jj * 8);
-          const float4 val = make_float4(wa * a.x + wb * o[md][4 * jj], wa * a.y + wb * o[md][4 * jj + 1],
-                                         wa * a.z + wb * o[md][4 * jj + 2], wa * a.w + wb * o[md][4 * jj + 3]);
-          if (p.mode == 1) {
-            *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
-          } else {
-            uint2 pk;
-            pk.x = pack2_bf16(val.x, val.y);
-            pk.y = pack2_bf16(val.z, val.w);
-            *reinterpret_cast<uint2*>(out_row + md * 32 + jj * 8) = pk;
-          }
-        }
-      if (g == 0) {
-        if (p.mode == 1)
-          *lrow = lm;
-        else
-          p.lse_out[(long long)head * p.ld_lse_out + t] = lm;
-      }
-    }
-  }
+  if (qrow < ql) step_epilogue<D>(p, st.o[si], st.lse[si], qs + qrow, head, g, o, m_run, lt);
 }
 
 // Padding rows of the final output: out 0, LSE -inf (every valid row is
