@@ -77,3 +77,56 @@ def test_share_past_2gib():
     H.compare_bf16("dk", _bits(dks[r].index_select(0, kidx)[:, [0, hkv - 1]]), dk)
     H.compare_bf16("dv", _bits(dvs[r].index_select(0, kidx)[:, [0, hkv - 1]]), dv)
     meta.close()
+
+
+def test_work_lists_past_sort_cap():
+    """One 600000-token sequence at CP = 1 (one head of 64): 4688 forward and
+    4688 dK/dV work items in the step, more than the device sorts (lists of
+    up to 4096 items are ordered heaviest first, longer ones keep each
+    sequence's last tile first). Every item must still run exactly once: out /
+    LSE / dQ on sampled rows against the oracle, exact dK / dV of the last key
+    rows, and over all key rows the sums sum_j dV_j = sum_p dO_p and
+    sum_j dK_j = 0 (softmax rows sum to one and are shift invariant)."""
+    import torch
+    T, cp, r, hq, hkv, d = 600000, 1, 0, 1, 1, 64
+    scale = 1.0 / math.sqrt(d)
+    cu = np.array([0, T], dtype=np.int32)
+    meta = api.cp_attn_rank_metadata(H.dev_i32(cu), H.dev_i32(cu.copy()), cp, r, -1, T)
+    s = meta.summary
+    H.log(f"[long lists] T={T}: {int(s.tiles_fwd[0])} forward and {int(s.tiles_dkdv[0])} dK/dV work items")
+    assert int(s.tiles_fwd[0]) > 4096 and int(s.tiles_dkdv[0]) > 4096
+    g = {nm: synth.device_normal_bf16((T, h, d), seed) for nm, h, seed in
+         (("q", hq, 61), ("k", hkv, 62), ("v", hkv, 63), ("do", hq, 64))}
+    loc = {"q": g["q"], "do": g["do"], "k": [g["k"]], "v": [g["v"]], "t_alloc": T, "t_local": T}
+    host = {nm: _bits(t) for nm, t in g.items()}
+    bt = synth.PackedBatch(name="long-lists", seed=61, cu=cu, cup=cu.copy(), hq=hq, hkv=hkv, d=d, **host)
+    out, lse = H.run_fwd(meta, loc, bt, scale)
+    dq, dks, dvs = H.run_bwd(meta, loc, bt, scale, out, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095 * 128, 4096 * 128 + 5, T // 2, T - 2, T - 1],
+                                     rng.integers(0, T, 12)]))
+    H.log(f"[long lists] oracle: {rows.size} rows")
+    o, l, dqr = O.share_rows(host["q"], host["k"], host["v"], host["do"], cu, cu, cp, r, scale, rows, [0],
+                             want_dq=True)
+    ridx = torch.from_numpy(rows).to("cuda")
+    H.compare_bf16("out", _bits(out.index_select(0, ridx)[:, [0]]), o)
+    H.compare_lse("lse", lse[[0]][:, ridx].cpu().numpy(), l)
+    H.compare_bf16("dq", _bits(dq.index_select(0, ridx)[:, [0]]), dqr)
+    keys = np.arange(T - 6, T)
+    dk, dv = O.share_keys_dkdv(host["q"], host["k"], host["v"], host["do"], cu, cu, cp, r, scale, r, keys, [0])
+    kidx = torch.from_numpy(keys).to("cuda")
+    H.compare_bf16("dk", _bits(dks[0].index_select(0, kidx)[:, [0]]), dk)
+    H.compare_bf16("dv", _bits(dvs[0].index_select(0, kidx)[:, [0]]), dv)
+    f = H.bf16_bits_to_f64
+    sum_dv = f(_bits(dvs[0]))[:, 0].sum(axis=0)
+    ref_dv = f(host["do"])[:, 0].sum(axis=0)
+    assert np.abs(sum_dv - ref_dv).max() <= 1e-3 * np.sqrt((ref_dv ** 2).sum()) + 0.05
+    dk_all = f(_bits(dks[0]))[:, 0]
+    # sum_j dK_j vanishes up to the rounding of D = <dO, out> (bf16 out) and of
+    # each dK row: bound as in the full-size identities
+    e = 2.0 ** -8 * np.abs(f(host["do"])[:, 0] * f(_bits(out))[:, 0]).sum(axis=-1)
+    std = scale * np.sqrt(((f(host["q"])[:, 0] ** 2) * (e ** 2)[:, None]).sum(axis=0))
+    rnd = 2.0 ** -9 * np.sqrt((dk_all ** 2).sum(axis=0))
+    assert (np.abs(dk_all.sum(axis=0)) / (6 * std + 8 * rnd + 1e-6)).max() <= 1.0
+    meta.close()
