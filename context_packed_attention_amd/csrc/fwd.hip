@@ -33,9 +33,10 @@ struct FwdParams {
   long long ld_q, ld_kv;  // elements per row
   float scale, c_log2;    // softmax scale, scale * log2(e)
   long long ld_o, ld_lse;
-  // epilogue: 0 = write the step's normalised partial (o, lse); 1 = fold it
-  // into the accumulator (o, lse) through the log-sum-exp; 2 = fold it and
-  // write the result as the bf16 output and final LSE instead. acc_first /
+  // epilogue: 1 = fold the step's normalised partial into the accumulator
+  // (o, lse) through the log-sum-exp; 2 = fold it and write the result as
+  // the bf16 output and final LSE instead (the fused launch writes those
+  // itself). acc_first /
   // acc_second: whether the accumulator already holds rows of the first /
   // second chunk (earlier steps covered them).
   int mode, acc_first, acc_second;
@@ -47,8 +48,9 @@ struct FwdParams {
 
 // The ring steps of one launch: blocks [off[j], off[j + 1]) compute ring step
 // step[j] (kind kind[j]) against K / V shard k[j] / v[j], over its work items
-// items[j], into o[j] (fp32 [rows, hq, D]: the step's partial, or the running
-// accumulator) and lse[j] (fp32 [hq, ld_lse]).
+// items[j], folding into the running accumulator o[j] (fp32 [rows, hq, D])
+// and lse[j] (fp32 [hq, ld_lse]); the fused launch runs every entry in each
+// block, over entry 0's work items, and needs no accumulator.
 struct FwdSteps {
   const uint16_t* k[CP_ATTN_MAX_CP];
   const uint16_t* v[CP_ATTN_MAX_CP];
@@ -61,9 +63,9 @@ struct FwdSteps {
   int n;
 };
 
-// A step's normalised partial for one lane's query row (local row t): mode 0
-// writes it, mode 1 folds it into the accumulator through the log-sum-exp,
-// mode 2 folds it and writes the bf16 output and the final LSE instead:
+// A step's normalised partial for one lane's query row (local row t): mode 1
+// folds it into the accumulator through the log-sum-exp, mode 2 folds it and
+// writes the bf16 output and the final LSE instead:
 //   out = (e^(la-m) out_a + e^(lb-m) out_b) / (e^(la-m) + e^(lb-m)),
 //   lse = m + log of that sum, m = max(la, lb).
 template <int D>
@@ -80,18 +82,6 @@ __device__ __forceinline__ void step_epilogue(const FwdParams& p, float* o_part,
   }
   float* orow = o_part + (long long)t * p.ld_o + head * D + g * 4;
   float* lrow = l_part + (long long)head * p.ld_lse + t;
-  if (p.mode == 0) {
-#pragma unroll
-    for (int md = 0; md < NMD; ++md)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float4 val = make_float4(o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
-                                 o[md][4 * jj + 3] * inv);
-        *reinterpret_cast<float4*>(orow + md * 32 + jj * 8) = val;
-      }
-    if (g == 0) *lrow = lse;
-    return;
-  }
   const bool has = (p.rowflags[t] & RF_SECOND) ? p.acc_second : p.acc_first;
   const float la = has ? *lrow : NEG_INF_F;
   const float mx = fmaxf(la, lse);

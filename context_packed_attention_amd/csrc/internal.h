@@ -90,7 +90,7 @@ struct cp_attn_meta {
 namespace cpattn {
 
 // side streams of the calling thread (streams.hip)
-constexpr int MAX_SIDE = 4;
+constexpr int MAX_SIDE = 1;
 struct SideSet {
   bool ready = false;
   hipStream_t s[MAX_SIDE] = {};

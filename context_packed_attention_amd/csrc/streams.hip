@@ -1,12 +1,13 @@
-// Side streams for running independent launches of one call concurrently:
-// per calling thread and device, a few streams of default priority with a
+// Side streams for running independent launches of one call concurrently
+// (the backward of short shares runs its dK/dV launch beside its dQ launch):
+// per calling thread and device, MAX_SIDE streams of default priority with a
 // fork event and one join event each, created on first use and never
 // released (a thread-exit hook could run after the HIP runtime has shut down
 // at process exit; each thread that calls the library on a device holds
-// four streams and five events there until the process ends). A fork is an event recorded on the caller's stream that
-// the side streams wait on; a join records an event on every side stream
-// that the caller's stream waits on (graph capture records the same pattern
-// as a fork and a join).
+// MAX_SIDE streams and MAX_SIDE + 1 events there until the process ends). A
+// fork is an event recorded on the caller's stream that the side streams wait
+// on; a join records an event on every side stream that the caller's stream
+// waits on (graph capture records the same pattern as a fork and a join).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
