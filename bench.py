@@ -678,30 +678,66 @@ def main():
     # A step = this batch's metadata, forward and backward. The metadata comes
     # from the host copies of cu_seqlens (the batch's lengths are on the host,
     # where a data loader makes them) through the path that needs no host
-    # synchronisation; packs of more sequences than it carries use the device
-    # path. The device path's step time is reported beside it.
+    # synchronisation, on a second stream (default priority), one step ahead:
+    # the next batch's tables are built while this one computes, and an event
+    # orders its forward after them, as a data loader feeding a training loop
+    # would. Every one of the K steps still builds its metadata inside the
+    # timed region. Packs of more sequences than the host path carries use the
+    # device path, in line. The in-line host-path and device-path step times
+    # are reported beside it.
     cu_h = np.asarray(batch.cu, dtype=np.int32)
     cup_h = np.asarray(batch.cup, dtype=np.int32)
     host_meta = len(cu_h) - 1 <= 255
+    meta_stream = torch.cuda.Stream()
 
-    def make_meta(host):
+    def make_meta(host, strm=None):
+        strm = stream if strm is None else strm
         if host:
-            return api.cp_attn_rank_metadata_host(cu_h, cup_h, cp, rank, -1, t_alloc, stream=stream)
-        return api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=stream)
+            return api.cp_attn_rank_metadata_host(cu_h, cup_h, cp, rank, -1, t_alloc, stream=strm)
+        return api.cp_attn_rank_metadata(cu, cup, cp, rank, -1, t_alloc, stream=strm)
 
-    def one_step(host=host_meta):
-        m = make_meta(host)
+    def fwd_bwd(m):
         api.cp_attn_fwd(m, q, ks, vs, hq, hkv, d, scale, 1, out, lse, ws_f, stream=stream)
         api.cp_attn_bwd(m, q, ks, vs, out, lse, do, hq, hkv, d, scale, 1, dq, dks, dvs, ws_b, stream=stream)
-        return m
 
+    def run_pass(n, held, how):
+        """how: 'pipelined' (host path, one step ahead), 'host' or 'device' (in line)."""
+        if how != "pipelined":
+            for _ in range(n):
+                m = make_meta(how == "host")
+                fwd_bwd(m)
+                held.append(m)
+            return
+        m = make_meta(True, meta_stream)
+        ev = torch.cuda.Event()
+        ev.record(meta_stream)
+        for k in range(n):
+            stream.wait_event(ev)
+            fwd_bwd(m)
+            held.append(m)
+            if k + 1 < n:
+                m = make_meta(True, meta_stream)
+                ev = torch.cuda.Event()
+                ev.record(meta_stream)
+
+    def timed_pass(how):
+        held = []
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        run_pass(args.steps, held, how)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        for m in held:
+            m.close()
+        return t, t + dt
+
+    main_how = "pipelined" if host_meta else "device"
     log(f"[bench] warmup {args.warmup}")
     held = []
-    for _ in range(args.warmup):
-        held.append(one_step())
-    # the timed passes hold every step's handle until they end; the library
-    # pools the handles' device buffers, so K of them are built and freed
-    # here first (untimed), as a training loop's first steps would
+    run_pass(args.warmup, held, main_how)
+    # the passes hold every step's handle until they end; the library pools
+    # the handles' device buffers, so K of them are built and freed here first
+    # (untimed), as a training loop's first steps would
     held += [make_meta(host_meta) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for m in held:
@@ -712,34 +748,24 @@ def main():
     # several percent of a step)
     api.cp_attn_timing_enable(True)
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        held.append(one_step())
+    run_pass(args.steps, held, main_how)
     torch.cuda.synchronize()
     api.cp_attn_timing_enable(False)
     per_kernel = api.cp_attn_timing_read()
     for m in held:
         m.close()
     held.clear()
-    # the same steps with the device metadata path (one host wait per step)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        held.append(one_step(False))
-    torch.cuda.synchronize()
-    device_meta_ms = (time.perf_counter() - t2) * 1e3 / args.steps
-    for m in held:
-        m.close()
-    held.clear()
-    # the timed pass, last: the two passes above keep the GPU busy before it
+    # the same steps with the metadata built in line: device path (one host
+    # wait per step), and host path
+    a, b = timed_pass("device")
+    device_meta_ms = (b - a) * 1e3 / args.steps
+    inline_host_ms = None
+    if host_meta:
+        a, b = timed_pass("host")
+        inline_host_ms = (b - a) * 1e3 / args.steps
+    # the timed pass, last: the passes above keep the GPU busy before it
     log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        held.append(one_step())
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for m in held:
-        m.close()
+    t0, t1 = timed_pass(main_how)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
@@ -843,8 +869,9 @@ def main():
                    "pairs": pairs, "step_pairs": step_pairs, "flops_per_step": flops_step, "t_alloc": t_alloc,
                    "parallelism": "one CP rank's share, all ring steps on one GPU"},
         "metadata_call_ms": round(sorted(meta_ms)[len(meta_ms) // 2], 4),
-        "metadata": ("host copies of cu_seqlens, no host synchronisation" if host_meta else "device path") +
-                    "; built every step inside the timed region",
+        "metadata": ("host copies of cu_seqlens, no host synchronisation, built on a second stream one step "
+                     "ahead" if host_meta else "device path, in line") + "; built every step inside the timed region",
+        "ms_per_step_host_metadata_inline": None if inline_host_ms is None else round(inline_host_ms, 4),
         "ms_per_step_device_metadata": round(device_meta_ms, 4),
         "kernels": kernels,
         "roofline": roof,
