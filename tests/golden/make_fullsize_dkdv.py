@@ -1,7 +1,8 @@
 """Write fullsize_dkdv.npz: exact dK / dV of sampled key rows of every source
 shard's part, at the two full-size shares the benchmark runs (the 131072-token
 GQA share, CP = 4, rank 2, and the 64K hierarchical pack's p2p share, CP = 2,
-rank 0), for one KV head each.
+rank 0), for one KV head each, and the exact LSE of every query row of the
+rank for that KV head's query heads (a by-product of the first pass).
 
 Calls only the oracle (its two-pass key-row helper) and the seeded input
 generator; nothing comes from the HIP path. The inputs the values depend on
@@ -67,6 +68,10 @@ def main():
         pre = f"w{cfg}_"
         arrays[pre + "meta"] = np.array([cp, r, g], dtype=np.int64)
         arrays[pre + "digest"] = np.array(input_digest(bt, g))
+        # every valid query row's LSE for the group's heads, at the rank's local rows
+        _, local = O.owner_map(bt.cu, bt.cup, cp)
+        arrays[pre + "lse_rows"] = local[stats["rows"]].astype(np.int32)
+        arrays[pre + "lse"] = stats["lse"].astype(np.float32)
         for s in range(cp):
             rows = key_rows(t_local, bt.cu, bt.cup, cp, s)
             dk, dv, dks, dvs = O.share_keys_dkdv_two_pass(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale,

@@ -2,7 +2,9 @@
 matches the seeded input generator (digest of the inputs its values depend
 on), and its values agree with the oracle's one-pass key-row routine on the
 key rows that routine computes cheaply (those few of the rank's queries
-reach), an independent path to the same numbers."""
+reach), an independent path to the same numbers; its every-row LSE agrees
+with the oracle's single-row routine on sampled rows and covers every local
+row of the rank once."""
 import math
 import os
 
@@ -39,3 +41,21 @@ def test_fixture_matches_generator_and_one_pass_oracle(cfg):
         for name in ("dk", "dv", "dk_sd", "dv_sd"):
             a = fx[pre + f"s{s}_{name}"]
             assert a.shape == (rs.size, bt.d) and np.isfinite(a).all()
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_fixture_lse_rows(cfg):
+    fx = np.load(OUT, allow_pickle=False)
+    bt, w = synth.make_workload(cfg)
+    pre = f"w{cfg}_"
+    cp, r, g = (int(x) for x in fx[pre + "meta"])
+    group = bt.hq // bt.hkv
+    rows, lse = fx[pre + "lse_rows"], fx[pre + "lse"]
+    t_local = bt.total_rows // cp
+    valid = O.valid_mask(bt.cu, bt.cup)[O.shard_rows(bt.cu, bt.cup, cp, r)]
+    assert np.array_equal(np.sort(rows), np.nonzero(valid)[0]) and lse.shape == (group, rows.size)
+    pick = np.random.default_rng(9).choice(rows.size, 6, replace=False)
+    heads = list(range(g * group, (g + 1) * group))
+    l = O.share_rows(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, 1.0 / math.sqrt(bt.d), rows[pick], heads)[1]
+    np.testing.assert_allclose(lse[:, pick], l, rtol=1e-6, atol=1e-5)
+    assert rows.max() < t_local

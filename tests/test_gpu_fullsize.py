@@ -2,7 +2,8 @@
 the 64K hierarchical-pack share), in the same launch configuration.
 
 The whole share is too large for the oracle, so: out / LSE / dQ are checked on
-sampled rows (each row one full softmax row of the oracle); dK / dV element by
+sampled rows (each row one full softmax row of the oracle), and the LSE of every
+row for one KV head's query heads against stored oracle values; dK / dV element by
 element on key rows at the start, middle and end of every source shard's part
 (so every ring step's launch, the causal one included, and key rows that all
 of the rank's queries reach), against values the oracle's two-pass helper
@@ -119,6 +120,24 @@ def test_dkdv_every_shard_vs_oracle_fixture(full):
         b = H.compare_bf16(f"dv[{s}] rows", res["dv"][s][rows][:, g], fx[pre + f"s{s}_dv"], sd=fx[pre + f"s{s}_dv_sd"])
         H.log(f"    dk max {a['max_abs']:.2e} (max |ref| {a['max_ref']:.3f}), dv max {b['max_abs']:.2e} "
               f"(max |ref| {b['max_ref']:.3f})")
+
+
+def test_lse_every_row_vs_oracle_fixture(full):
+    """The LSE of every query row of the rank for one KV head's query heads,
+    against the oracle's values stored beside the dK / dV fixture."""
+    from tests.golden.make_fullsize_dkdv import input_digest
+    bt, w, r, scale, res = full
+    cfg = 4 if bt.hkv != bt.hq else 5
+    fx = np.load(FIXTURE, allow_pickle=False)
+    pre = f"w{cfg}_"
+    cp, rank, g = (int(x) for x in fx[pre + "meta"])
+    assert (cp, rank) == (w["cp"], r)
+    assert str(fx[pre + "digest"]) == input_digest(bt, g), "fixture is stale: rerun tests/golden/make_fullsize_dkdv.py"
+    group = bt.hq // bt.hkv
+    heads = list(range(g * group, (g + 1) * group))
+    rows = fx[pre + "lse_rows"]
+    H.log(f"[full] LSE of {rows.size} rows x {group} heads vs the fixture")
+    H.compare_lse("lse every row", res["lse"][heads][:, rows], fx[pre + "lse"].astype(np.float64))
 
 
 def _tol(vals):
