@@ -100,8 +100,13 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   constexpr int BM = FWD_BM, BN = 64;
   constexpr int NKK = D / 16, NMD = D / 32;
   using KCopy = TileCopy<D, false, BN, NWAVES, true>;  // K read both ways: permuted rows (V too, same plan)
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][KCopy::BYTES / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][KCopy::BYTES / 2];
+  // one LDS array per buffer (its K tile, then its V tile), always named
+  // statically, so the compiler sees that this tile's reads cannot touch the
+  // buffer whose copy is in flight
+  __shared__ __attribute__((aligned(1024))) uint16_t T0[KCopy::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint16_t T1[KCopy::BYTES];
+  auto ks_of = [&](auto b) { return decltype(b)::value ? T1 : T0; };
+  auto vs_of = [&](auto b) { return (decltype(b)::value ? T1 : T0) + KCopy::BYTES / 2; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -167,19 +172,22 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
     v.vb = st.v[i] + kvs * p.ld_kv + kvh * D;
     return v;
   };
-  auto issue = [&](const View& v, int kt, int buf) {
+  auto issue = [&](const View& v, int kt, auto buf) {
     const long long off = (long long)kt * BN * ldb, end = (long long)v.kl * ldb;
-    kc.copy(rsrc_from(v.kb, off, end), Ks[buf], w);
-    kc.copy(rsrc_from(v.vb, off, end), Vs[buf], w);
+    kc.copy(rsrc_from(v.kb, off, end), ks_of(buf), w);
+    kc.copy(rsrc_from(v.vb, off, end), vs_of(buf), w);
   };
   // the first step with work, then (step, tile) in order
   int i = 0;
   View cur = view(0);
   while (cur.nt == 0 && i + 1 < st.n) cur = view(++i);
-  if (cur.nt > 0) issue(cur, 0, 0);
+  if (cur.nt > 0) issue(cur, 0, Buf<0>{});
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
-  int kt = 0, it = 0;
-  while (cur.nt > 0) {
+  int kt = 0;
+  // one tile in buffer `buf` (the loop below alternates the buffers); every
+  // next tile's copy goes to the other buffer, which the next tile's barrier
+  // publishes
+  auto tile_step = [&](auto buf) {
     // the tile after this one, possibly the next step's first
     int ni = i, nkt = kt + 1;
     View nxt = cur;
@@ -189,7 +197,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
       while (nxt.nt == 0 && ni + 1 < st.n) nxt = view(++ni);
     }
     const bool more = nxt.nt > 0;
-    const int buf = it & 1;
+    const Buf<1 - decltype(buf)::value> other{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int k0 = kt * BN;
@@ -197,7 +205,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
     // the next tile's copy is issued after this tile's score products (the
     // address arithmetic then fills the wait for their results); idle
     // wavefronts issue their share at once
-    if (!active && more) issue(nxt, nkt, buf ^ 1);
+    if (!active && more) issue(nxt, nkt, other);
     if (active) {
       // rows outside this step's query range take no part in it
       const float lse2 = (qrow >= cur.rlo && qrow < cur.rhi) ? lse2_row : __builtin_huge_valf();
@@ -211,9 +219,9 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          s[mb] = mfma32x32x16(lds_read_row<D, true>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
+          s[mb] = mfma32x32x16(lds_read_row<D, true>(ks_of(buf), mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
       }
-      if (more) issue(nxt, nkt, buf ^ 1);
+      if (more) issue(nxt, nkt, other);
       if (cur.causal && k0 + BN - 1 > wrow_lo) {
         // keys after the lane's row (a real branch, kept out of
         // if-conversion; only the tiles on a wavefront's diagonal take it)
@@ -231,7 +239,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          dp[mb] = mfma32x32x16(lds_read_row<D, true>(Vs[buf], mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
+          dp[mb] = mfma32x32x16(lds_read_row<D, true>(vs_of(buf), mb * 32 + l32, 2 * kk + g), df[kk], dp[mb]);
 #pragma unroll
         for (int e = 0; e < 32 / NKK; ++e) {
           const int j = kk * (32 / NKK) + e;
@@ -247,18 +255,22 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
         const bf16x8_t ds = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
 #pragma unroll
         for (int md = 0; md < NMD; ++md)
-          acc[md] = mfma32x32x16(lds_read_tr<D, false, true>(Ks[buf], kk2 * 16, md * 32, lane), ds, acc[md]);
+          acc[md] = mfma32x32x16(lds_read_tr<D, false, true, true>(ks_of(buf), kk2 * 16, md * 32, lane), ds, acc[md]);
       }
     }
     i = ni;
     kt = nkt;
     cur = nxt;
-    ++it;
+  };
+  while (cur.nt > 0) {
+    tile_step(Buf<0>{});
+    if (cur.nt == 0) break;
+    tile_step(Buf<1>{});
   }
   // bf16 dQ through LDS (the K tiles are free), whole-row stores
   constexpr int SP = D * 2 + 16;
-  static_assert(BM * SP <= (int)sizeof(Ks), "dQ staging fits the K tiles");
-  char* const stage = reinterpret_cast<char*>(&Ks[0][0]);
+  static_assert(BM * SP <= (int)sizeof(T0), "dQ staging fits one buffer");
+  char* const stage = reinterpret_cast<char*>(&T0[0]);
   __syncthreads();  // every wavefront is done with the K and V tiles
   stage_row_bf16<D>(stage + (w * 32 + l32) * SP, g, acc, p.scale);
   __syncthreads();

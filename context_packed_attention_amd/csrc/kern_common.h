@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cpattn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -199,6 +201,14 @@ __host__ __device__ constexpr int tile_rowb() { return TR_ONLY ? (D == 128 ? 320
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+// A double buffer's index as a compile-time constant: kernels that name
+// each buffer's LDS array statically let the compiler see that reads of one
+// buffer cannot touch the other, whose copy is in flight, so it does not
+// wait for that copy before them (with one array indexed by the buffer
+// number it must).
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
 // Direct global->LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
 // lane l of the wavefront writes LDS bytes [chunk + 16 l, chunk + 16 l + 16).
 // Offsets at or past the resource's num_records read as zeros.
@@ -284,14 +294,26 @@ __device__ __forceinline__ bf16x8_t lds_read_row(const uint16_t* tile, int row, 
 // hardware hands lane j column j of those four rows.
 // In a permuted tile (PERM) logical rows k0 + 4 g + (i / 4) and k0 + 8 + 4 g +
 // (i / 4) sit at physical rows k0 + 4 (i / 4) + g and 2 rows further on.
-template <int D, bool TR_ONLY, bool PERM = false>
+template <int D, bool TR_ONLY, bool PERM = false, bool OPAQUE = TR_ONLY>
 __device__ __forceinline__ bf16x8_t lds_read_tr(const uint16_t* tile, int k0, int col0, int lane) {
   static_assert(!(PERM && TR_ONLY), "permuted tiles use the row-read stride");
   constexpr int ROWB = tile_rowb<D, TR_ONLY>();
   const int i = lane & 15, h = (lane >> 4) & 1, g = lane >> 5;
-  const int col = col0 + 16 * h + 4 * (i & 3);
-  const int r0 = PERM ? k0 + 4 * (i >> 2) + g : k0 + 4 * g + (i >> 2);
-  const char* base = reinterpret_cast<const char*>(tile) + r0 * ROWB + col * 2;
+  const char* base;
+  if constexpr (OPAQUE) {
+    // the lane's offset as one opaque value (computed once) plus a constant
+    // per read: each address is then a short chain of additions from the
+    // tile, short enough for the compiler to see which LDS array the read
+    // touches, so it waits only for copies into that array (the forward's
+    // V tiles and dQ's K tiles; measured neutral to slower on dK/dV's)
+    int lane_off = (PERM ? 4 * (i >> 2) + g : 4 * g + (i >> 2)) * ROWB + (16 * h + 4 * (i & 3)) * 2;
+    __asm__("" : "+v"(lane_off));
+    base = reinterpret_cast<const char*>(tile) + lane_off + (k0 * ROWB + col0 * 2);
+  } else {
+    const int col = col0 + 16 * h + 4 * (i & 3);
+    const int r0 = PERM ? k0 + 4 * (i >> 2) + g : k0 + 4 * g + (i >> 2);
+    base = reinterpret_cast<const char*>(tile) + r0 * ROWB + col * 2;
+  }
   i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(base));
   i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4_t*)(base + (PERM ? 2 : 8) * ROWB));
