@@ -115,8 +115,15 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   map_block(blockIdx.x, p.hq, item, head);
   const int sb = p.items[2 * item], tile = p.items[2 * item + 1];
   const int B = p.B;
-  // step tables: [step][q_start, q_len, kv_start, kv_len][sequence]
-  auto tab = [&](int i, int f) { return p.steps[(long long)i * 4 * B + f * B + sb]; };
+  // step tables: [step][q_start, q_len, kv_start, kv_len][sequence], read
+  // once into LDS: moving on to the next step mid-loop then reads LDS and
+  // does not wait for the tile copies in flight (a global read would: the
+  // load counter retires in order)
+  __shared__ int step_tab[4 * CP_ATTN_MAX_CP];
+  for (int i = 0; i < st.n; ++i)
+    if (tid < 4) step_tab[4 * i + tid] = p.steps[(long long)i * 4 * B + tid * B + sb];
+  __syncthreads();
+  auto tab = [&](int i, int f) { return step_tab[4 * i + f]; };
   const int base = tab(0, 0), ql0 = tab(0, 1);  // the causal step covers every valid row of the slot
   const int q0 = tile * BM;
   const int nq = min(BM, ql0 - q0);

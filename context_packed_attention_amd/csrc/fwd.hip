@@ -162,8 +162,23 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   int item, head;
   map_block((int)blockIdx.x - st.off[si], p.hq, item, head);
   const int sb = st.items[si][2 * item], tile = st.items[si][2 * item + 1];
-  // entry j's sequence tables: [step][q_start, q_len, kv_start, kv_len][B]
-  auto tab = [&](int j, int f) { return p.steps[((long long)st.step[j] * 4 + f) * p.B + sb]; };
+  // entry j's sequence tables: [step][q_start, q_len, kv_start, kv_len][B].
+  // FUSED: every entry's four values are read once into LDS, so moving on
+  // to the next entry mid-loop reads LDS and does not wait for the tile
+  // copies in flight (a global read would: the load counter retires in
+  // order)
+  __shared__ int ent_tab[FUSED ? 4 * CP_ATTN_MAX_CP : 1];
+  if constexpr (FUSED) {
+    for (int j = 0; j < st.n; ++j)
+      if (tid < 4) ent_tab[4 * j + tid] = p.steps[((long long)st.step[j] * 4 + tid) * p.B + sb];
+    __syncthreads();
+  }
+  auto tab = [&](int j, int f) {
+    if constexpr (FUSED)
+      return ent_tab[4 * j + f];
+    else
+      return p.steps[((long long)st.step[j] * 4 + f) * p.B + sb];
+  };
   const int qs = tab(si, 0), ql = tab(si, 1);  // the block's rows are relative to qs
   const int q0 = tile * BM;
   const int nq = min(BM, ql - q0);
