@@ -122,9 +122,9 @@ __device__ __forceinline__ void step_epilogue(const FwdParams& p, float* o_part,
 }
 
 // One block = NWAVES wavefronts (FWD_BM query rows) of one head; each wavefront owns
-// 32 query rows. K and V tiles of 64 rows are copied straight from global
-// memory into padded LDS tiles (buffer loads with the lds modifier, no
-// register staging), double-buffered. Scores are computed transposed
+// 32 query rows. K and V tiles of BN rows (64; 32 in the fused launch) are
+// copied straight from global memory into padded LDS tiles (buffer loads
+// with the lds modifier, no register staging), double-buffered. Scores are computed transposed
 // (S^T = K Q^T, K rows as the A operand) so each lane owns one query row: the
 // online softmax needs one cross-lane max per tile, and O^T = V^T P^T takes
 // V^T through transposing LDS reads and keeps per-lane row scaling. Keys past
@@ -140,11 +140,12 @@ __device__ __forceinline__ void step_epilogue(const FwdParams& p, float* o_part,
 // the next and the log-sum-exp merge of the steps happens in registers; the
 // epilogue writes the bf16 output and the final LSE. Rows outside an entry's
 // query range take no part in it (masked).
-template <int D, bool FUSED>
-__global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(FwdParams p, FwdSteps st) {
-  constexpr int BM = FWD_BM, BN = 64;
+template <int D, bool FUSED, int BN>
+__global__ void __launch_bounds__(BLOCK_THREADS, BN == 32 ? 3 : 8 / NWAVES) fwd_step_kernel(FwdParams p, FwdSteps st) {
+  constexpr int BM = FWD_BM;
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
+  constexpr int MB = BN / 32, KK2 = BN / 16;  // 32-key score blocks, 16-key P V slices per tile
   using KCopy = TileCopy<D, false, BN, NWAVES>;
   using VCopy = TileCopy<D, true, BN, NWAVES>;
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][KCopy::BYTES / 2];
@@ -251,22 +252,22 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
   // bf16; masking runs only on a wavefront's last tiles (keys past the
   // range, or at the causal step keys after its first row) and, fused, on
   // the tiles of entries whose query range splits the wavefront's rows
-  auto key_tile = [&](const Cur& u, int buf, bool masked, bf16x8_t (&pb)[4], bf16x8_t (&vf)[4][NMD]) {
+  auto key_tile = [&](const Cur& u, int buf, bool masked, bf16x8_t (&pb)[KK2], bf16x8_t (&vf)[KK2][NMD]) {
     const int k0 = u.kt * BN;
-    f32x16_t s[2];
-    s[0] = zero16();
-    s[1] = zero16();
+    f32x16_t s[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) s[mb] = zero16();
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
         s[mb] = mfma32x32x16(lds_read_row<D>(Ks[buf], mb * 32 + l32, 2 * kk + g), qf[kk], s[mb]);
     }
     // all V fragments of the tile are read now, so the LDS latency hides
     // behind the softmax instead of stalling the P V products (the
     // scheduling fence keeps the compiler from sinking the reads again)
 #pragma unroll
-    for (int kk2 = 0; kk2 < 4; ++kk2)
+    for (int kk2 = 0; kk2 < KK2; ++kk2)
 #pragma unroll
       for (int md = 0; md < NMD; ++md) vf[kk2][md] = lds_read_tr<D, true>(Vs[buf], kk2 * 16, md * 32, lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -275,7 +276,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       __asm__ volatile("" ::: "memory");
       const bool row_in = !FUSED || (qrow >= u.rlo && qrow < u.rhi);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
@@ -285,7 +286,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     }
     float mx = NEG_INF_F;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
     mx = max_halves(mx);
@@ -302,7 +303,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     const float base = (m_run == NEG_INF_F) ? 0.f : m_run * c;
     float lsum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float pv = fast_exp2(fmaf(s[mb][j], c, -base));
@@ -311,12 +312,12 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
       }
     l_run += lsum;
 #pragma unroll
-    for (int kk2 = 0; kk2 < 4; ++kk2) pb[kk2] = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
+    for (int kk2 = 0; kk2 < KK2; ++kk2) pb[kk2] = pack8_bf16(s[kk2 >> 1], 8 * (kk2 & 1));
   };
   // second half: O += P V from registers
-  auto pv_tile = [&](const bf16x8_t (&pb)[4], const bf16x8_t (&vf)[4][NMD]) {
+  auto pv_tile = [&](const bf16x8_t (&pb)[KK2], const bf16x8_t (&vf)[KK2][NMD]) {
 #pragma unroll
-    for (int kk2 = 0; kk2 < 4; ++kk2)
+    for (int kk2 = 0; kk2 < KK2; ++kk2)
 #pragma unroll
       for (int md = 0; md < NMD; ++md) o[md] = mfma32x32x16(vf[kk2][md], pb[kk2], o[md]);
   };
@@ -351,7 +352,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     const bool rows_all = wrow_lo >= cur.rlo && wrow_last < cur.rhi;
     const bool active = rows_any && !(cur.causal && k0 > wrow_hi);
     const bool need_mask = (k0 + BN > cur.kl) || (cur.causal && k0 + BN - 1 > wrow_lo) || !rows_all;
-    bf16x8_t pb[4], vf[4][NMD];
+    bf16x8_t pb[KK2], vf[KK2][NMD];
     if (active) key_tile(cur, buf, need_mask, pb, vf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -368,14 +369,23 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) fwd_step_kernel(Fwd
     // every step is in: the bf16 output (through LDS, whole-row stores; the
     // K tiles are free) and the final LSE
     constexpr int SP = D * 2 + 16;
-    static_assert(FWD_BM * SP <= (int)sizeof(Ks), "output staging fits the K tiles");
-    char* const stage = reinterpret_cast<char*>(&Ks[0][0]);
+    // rows [0, FWD_BM / 2) stage in the K tiles, the rest in the V tiles
+    constexpr int HALF = FWD_BM / 2;
+    static_assert(HALF * SP <= (int)sizeof(Ks) && HALF * SP <= (int)sizeof(Vs), "output staging fits the tiles");
+    auto srow = [&](int r) {
+      return r < HALF ? reinterpret_cast<char*>(&Ks[0][0]) + r * SP : reinterpret_cast<char*>(&Vs[0][0]) + (r - HALF) * SP;
+    };
     __syncthreads();  // every wavefront is done with the K and V tiles
-    stage_row_bf16<D>(stage + (w * 32 + l32) * SP, g, o, lt > 0.f ? 1.f / lt : 0.f);
+    stage_row_bf16<D>(srow(w * 32 + l32), g, o, lt > 0.f ? 1.f / lt : 0.f);
     if (qrow < ql && g == 0)
       p.lse_out[(long long)head * p.ld_lse_out + qs + qrow] = lt > 0.f ? m_run * p.scale + __logf(lt) : NEG_INF_F;
     __syncthreads();
-    store_rows<D, SP, BLOCK_THREADS>(stage, nq, p.out + (long long)(qs + q0) * p.ld_o + head * D, p.ld_o, tid);
+    uint16_t* const dst = p.out + (long long)(qs + q0) * p.ld_o + head * D;
+    constexpr int UPR = D * 2 / 16;
+    for (int u = tid; u < nq * UPR; u += BLOCK_THREADS) {
+      const int r = u / UPR, cc = u - r * UPR;
+      *reinterpret_cast<uint4*>(dst + (long long)r * p.ld_o + cc * 8) = *reinterpret_cast<const uint4*>(srow(r) + cc * 16);
+    }
     return;
   }
   if (qrow < ql) step_epilogue<D>(p, st.o[si], st.lse[si], qs + qrow, head, g, o, m_run, lt);
@@ -400,6 +410,13 @@ __global__ void __launch_bounds__(256) pad_rows_kernel(const int32_t* __restrict
 // Whether the forward runs every ring step in one fused launch (each block
 // through all steps, merged in registers): when the steps' own launches
 // would be short.
+// Key rows per tile of the fused launch: 32-key tiles take 168 VGPRs and
+// 41 KB of LDS, so three blocks share a CU (two with 64-key tiles); short
+// shares are latency-bound and gain from the third (1.7-2.1% per step on
+// the 16K packs), long ones lose (the per-tile costs double), so the
+// per-step launches keep 64.
+constexpr int FWD_BN_FUSED = 32;
+
 static bool fwd_fused(const cp_attn_meta* m, int hq) {
   if (m->cp < 2) return false;
   long long mx = 0;
@@ -428,14 +445,14 @@ static cp_attn_status launch_fwd_steps(const cp_attn_meta* m, const FwdParams& p
   timing_begin(strm, fused ? "fwd_fused" : "fwd_step");
   if (d == 128) {
     if (fused)
-      hipLaunchKernelGGL((fwd_step_kernel<128, true>), grid, blk, 0, strm, p, st);
+      hipLaunchKernelGGL((fwd_step_kernel<128, true, FWD_BN_FUSED>), grid, blk, 0, strm, p, st);
     else
-      hipLaunchKernelGGL((fwd_step_kernel<128, false>), grid, blk, 0, strm, p, st);
+      hipLaunchKernelGGL((fwd_step_kernel<128, false, 64>), grid, blk, 0, strm, p, st);
   } else {
     if (fused)
-      hipLaunchKernelGGL((fwd_step_kernel<64, true>), grid, blk, 0, strm, p, st);
+      hipLaunchKernelGGL((fwd_step_kernel<64, true, FWD_BN_FUSED>), grid, blk, 0, strm, p, st);
     else
-      hipLaunchKernelGGL((fwd_step_kernel<64, false>), grid, blk, 0, strm, p, st);
+      hipLaunchKernelGGL((fwd_step_kernel<64, false, 64>), grid, blk, 0, strm, p, st);
   }
   timing_end(strm);
   return hip_check(hipGetLastError(), "fwd_step launch");
