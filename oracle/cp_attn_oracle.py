@@ -614,7 +614,7 @@ def share_keys_dkdv(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, s
 
 
 def group_row_stats(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float, kv_head: int,
-                    max_elems: int = 1 << 24) -> dict:
+                    max_elems: int = 1 << 24, proj=None) -> dict:
     """First pass of the exact dK / dV of chosen key rows at any size: for
     every valid query row p that rank r owns and every query head h of KV
     group ``kv_head``, the row's softmax statistics
@@ -626,11 +626,24 @@ def group_row_stats(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, s
     method) var_D_{p,h} = sum_d (dO out)^2 + sum_j (P_pj dP_pj)^2, the sum the
     rounding model of share_rounding_sd needs.
 
+    With ``proj`` (float64 [group, D], one vector u_h per query head of the
+    group) it also returns, per row, the projections of the row's exact
+    output and query gradient on u_h,
+
+        out_proj_{p,h} = <out_p,h, u_h>,   dq_proj_{p,h} = <dQ_p,h, u_h>,
+        dQ_p,h = scale sum_{j <= p} dS_pj K_j,   dS_pj = P_pj (dP_pj - D_p,h),
+
+    and, for the comparison tolerance only (not the method), the standard
+    deviations "out_proj_sd" and "dq_proj_sd" of those projections under the
+    rounding model of share_rounding_sd (P rounded before P V, dS before
+    dS K, D formed from the rounded output), taken along u_h: with u_h a
+    unit basis vector e_d they are that model's per-element deviations.
+
     Each softmax row is whole (keys 0..p of its sequence); the rows are only
     processed in batches of at most ``max_elems`` scores. Returns a dict with
     "rows" (global query rows, int64 [n]), "seq", "pos" (sequence and
     in-sequence position of each), and [group, n] float64 arrays "lse",
-    "dcoef", "var_d_terms".
+    "dcoef", "var_d_terms" (and the four projection arrays with ``proj``).
     """
     cu, cup = validate(cu, cup, cp, r)
     hq = q_bits.shape[1]
@@ -654,6 +667,9 @@ def group_row_stats(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, s
     lse = np.full((group, n), NEG_INF)
     dcoef = np.zeros((group, n))
     var_terms = np.zeros((group, n))
+    pnames = ("out_proj", "dq_proj", "out_proj_sd", "dq_proj_sd")
+    c_rnd = BF16_UNIT_ROUNDOFF ** 2 / 3.0
+    pj = {nm: np.zeros((group, n)) for nm in pnames} if proj is not None else None
     kf = bf16_to_f64(k_bits[:, kv_head])
     vf = bf16_to_f64(v_bits[:, kv_head])
     for jh, h in enumerate(range(kv_head * group, (kv_head + 1) * group)):
@@ -681,9 +697,22 @@ def group_row_stats(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, s
             lse[jh, i:j] = l
             dcoef[jh, i:j] = (dO * out).sum(axis=1)
             var_terms[jh, i:j] = ((dO * out) ** 2).sum(axis=1) + ((P * dP) ** 2).sum(axis=1)
+            if pj is not None:
+                u = np.asarray(proj[jh], dtype=np.float64)
+                Ku, Vu = K @ u, V @ u
+                dS = P * (dP - dcoef[jh, i:j][:, None])
+                pj["out_proj"][jh, i:j] = out @ u
+                pj["dq_proj"][jh, i:j] = scale * (dS @ Ku)
+                var_D = c_rnd * var_terms[jh, i:j]
+                pj["out_proj_sd"][jh, i:j] = np.sqrt(c_rnd * ((P ** 2) @ (Vu ** 2)))
+                pj["dq_proj_sd"][jh, i:j] = np.sqrt(c_rnd * scale ** 2 * ((dS ** 2) @ (Ku ** 2)) +
+                                                    scale ** 2 * var_D * (P @ Ku) ** 2)
             i = j
-    return {"rows": rows, "seq": seq, "pos": pos, "kv_head": kv_head, "group": group,
-            "lse": lse, "dcoef": dcoef, "var_d_terms": var_terms}
+    res = {"rows": rows, "seq": seq, "pos": pos, "kv_head": kv_head, "group": group,
+           "lse": lse, "dcoef": dcoef, "var_d_terms": var_terms}
+    if pj is not None:
+        res.update(pj)
+    return res
 
 
 def keys_dkdv_from_stats(stats: dict, q_bits, k_bits, v_bits, do_bits, cu, cup, scale: float, key_rows):

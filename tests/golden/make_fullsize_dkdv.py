@@ -2,7 +2,9 @@
 shard's part, at the two full-size shares the benchmark runs (the 131072-token
 GQA share, CP = 4, rank 2, and the 64K hierarchical pack's p2p share, CP = 2,
 rank 0), for one KV head each, and the exact LSE of every query row of the
-rank for that KV head's query heads (a by-product of the first pass).
+rank for that KV head's query heads (a by-product of the first pass), with
+every such row's output and query gradient projected on a seeded unit
+vector per head and the rounding model's deviation of each projection.
 
 Calls only the oracle (its two-pass key-row helper) and the seeded input
 generator; nothing comes from the HIP path. The inputs the values depend on
@@ -61,7 +63,10 @@ def main():
         g = bt.hkv - 1
         scale = 1.0 / math.sqrt(bt.d)
         t0 = time.time()
-        stats = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g)
+        group = bt.hq // bt.hkv
+        u = np.random.default_rng(7000 + cfg).standard_normal((group, bt.d))
+        u /= np.linalg.norm(u, axis=1, keepdims=True)
+        stats = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g, proj=u)
         print(f"{bt.name}: first pass over {stats['rows'].size} rows x {stats['group']} heads "
               f"in {time.time() - t0:.1f} s", flush=True)
         t_local = bt.total_rows // cp
@@ -72,6 +77,10 @@ def main():
         _, local = O.owner_map(bt.cu, bt.cup, cp)
         arrays[pre + "lse_rows"] = local[stats["rows"]].astype(np.int32)
         arrays[pre + "lse"] = stats["lse"].astype(np.float32)
+        # every such row's out and dQ projected on u (one vector per head)
+        arrays[pre + "proj_u"] = u
+        for nm in ("out_proj", "dq_proj", "out_proj_sd", "dq_proj_sd"):
+            arrays[pre + nm] = stats[nm].astype(np.float32)
         for s in range(cp):
             rows = key_rows(t_local, bt.cu, bt.cup, cp, s)
             dk, dv, dks, dvs = O.share_keys_dkdv_two_pass(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale,

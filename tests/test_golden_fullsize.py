@@ -2,9 +2,9 @@
 matches the seeded input generator (digest of the inputs its values depend
 on), and its values agree with the oracle's one-pass key-row routine on the
 key rows that routine computes cheaply (those few of the rank's queries
-reach), an independent path to the same numbers; its every-row LSE agrees
-with the oracle's single-row routine on sampled rows and covers every local
-row of the rank once."""
+reach), an independent path to the same numbers; its every-row LSE and
+projected out / dQ agree with the oracle's single-row routine on sampled
+rows and cover every valid local row of the rank once."""
 import math
 import os
 
@@ -56,6 +56,18 @@ def test_fixture_lse_rows(cfg):
     assert np.array_equal(np.sort(rows), np.nonzero(valid)[0]) and lse.shape == (group, rows.size)
     pick = np.random.default_rng(9).choice(rows.size, 6, replace=False)
     heads = list(range(g * group, (g + 1) * group))
-    l = O.share_rows(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, 1.0 / math.sqrt(bt.d), rows[pick], heads)[1]
+    o, l, dq = O.share_rows(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, 1.0 / math.sqrt(bt.d), rows[pick], heads,
+                            want_dq=True)
     np.testing.assert_allclose(lse[:, pick], l, rtol=1e-6, atol=1e-5)
     assert rows.max() < t_local
+    # every row's projected out / dQ: the oracle's single-row routine on the
+    # sampled rows, projected on the stored unit vectors
+    u = fx[pre + "proj_u"]
+    assert u.shape == (group, bt.d) and np.allclose(np.linalg.norm(u, axis=1), 1.0)
+    for name, ref in (("out_proj", o), ("dq_proj", dq)):
+        a = fx[pre + name]
+        assert a.shape == lse.shape and np.isfinite(a).all()
+        want = np.stack([ref[:, jh] @ u[jh] for jh in range(group)])
+        np.testing.assert_allclose(a[:, pick], want, rtol=1e-5, atol=1e-7)
+        sd = fx[pre + name + "_sd"]
+        assert sd.shape == lse.shape and np.isfinite(sd).all() and (sd >= 0).all()

@@ -2,8 +2,9 @@
 the 64K hierarchical-pack share), in the same launch configuration.
 
 The whole share is too large for the oracle, so: out / LSE / dQ are checked on
-sampled rows (each row one full softmax row of the oracle), and the LSE of every
-row for one KV head's query heads against stored oracle values; dK / dV element by
+sampled rows (each row one full softmax row of the oracle), and for every row
+of one KV head's query heads the LSE and the out and dQ rows projected on a
+fixed unit vector against stored oracle values; dK / dV element by
 element on key rows at the start, middle and end of every source shard's part
 (so every ring step's launch, the causal one included, and key rows that all
 of the rank's queries reach), against values the oracle's two-pass helper
@@ -138,6 +139,39 @@ def test_lse_every_row_vs_oracle_fixture(full):
     rows = fx[pre + "lse_rows"]
     H.log(f"[full] LSE of {rows.size} rows x {group} heads vs the fixture")
     H.compare_lse("lse every row", res["lse"][heads][:, rows], fx[pre + "lse"].astype(np.float64))
+
+
+def test_out_dq_every_row_projected_vs_oracle_fixture(full):
+    """The output and query gradient of every query row of the rank for one
+    KV head's query heads, projected on the stored unit vector of each head,
+    against the oracle's exact projections. Bar: the bf16 rounding of the
+    row's own elements (at most 2^-8 of each, weighted by |u_d|) plus six of
+    the rounding model's deviations of the projection (P rounded before
+    P V, dS before dS K, D formed from the rounded output), plus 1e-5 of the
+    row's norm for fp32 accumulation."""
+    bt, w, r, scale, res = full
+    cfg = 4 if bt.hkv != bt.hq else 5
+    fx = np.load(FIXTURE, allow_pickle=False)
+    pre = f"w{cfg}_"
+    cp, rank, g = (int(x) for x in fx[pre + "meta"])
+    group = bt.hq // bt.hkv
+    heads = list(range(g * group, (g + 1) * group))
+    rows = fx[pre + "lse_rows"]
+    u = fx[pre + "proj_u"]
+    for name, key in (("out", "out_proj"), ("dq", "dq_proj")):
+        got = H.bf16_bits_to_f64(res[name][rows][:, heads])  # [n, group, D]
+        ref, sd = fx[pre + key].astype(np.float64), fx[pre + key + "_sd"].astype(np.float64)
+        worst = 0.0
+        for jh in range(group):
+            gp = got[:, jh] @ u[jh]
+            tol = 2.0 ** -8 * (np.abs(got[:, jh]) @ np.abs(u[jh])) + 6.0 * sd[jh] + \
+                1e-5 * np.linalg.norm(got[:, jh], axis=1) + 1e-7
+            ratio = np.abs(gp - ref[jh]) / tol
+            worst = max(worst, float(ratio.max()))
+            bad = np.nonzero(ratio > 1.0)[0]
+            assert bad.size == 0, (f"{name} head {heads[jh]}: {bad.size} rows over the bar, first local row "
+                                   f"{int(rows[bad[0]])}: {gp[bad[0]]:.6g} vs {ref[jh, bad[0]]:.6g}")
+        H.log(f"[full] {name} projected on every row ({rows.size} x {group}): worst / bar {worst:.3f}")
 
 
 def _tol(vals):

@@ -227,3 +227,32 @@ def test_two_pass_stats_are_the_rows_softmax():
             np.testing.assert_allclose(st["lse"][jh], sh["lse"][h, idx], rtol=1e-12, atol=1e-12)
             dref = (O.bf16_to_f64(bt.do[st["rows"], h]) * sh["out"][idx, h]).sum(axis=1)
             np.testing.assert_allclose(st["dcoef"][jh], dref, rtol=1e-10, atol=1e-12)
+
+
+def test_row_projections_match_full_share():
+    """With projection vectors, the first pass's projected output and query
+    gradient of every rank row equal the full share's rows projected on the
+    same vectors, and along unit basis vectors its projected deviations are
+    the rounding model's per-element deviations (share_rounding_sd, computed
+    element by element on its own)."""
+    bt = _random_batch(43, 2, 3, 4, 2, 8, True)
+    scale, cp, r = 0.4, 2, 1
+    sh = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
+    sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
+    own = O.shard_rows(bt.cu, bt.cup, cp, r)
+    loc = {int(g): i for i, g in enumerate(own)}
+    rng = np.random.default_rng(5)
+    for g in range(2):
+        u = rng.standard_normal((2, 8))
+        st = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g, max_elems=40, proj=u)
+        idx = np.array([loc[int(x)] for x in st["rows"]])
+        for jh, h in enumerate(range(2 * g, 2 * g + 2)):
+            np.testing.assert_allclose(st["out_proj"][jh], sh["out"][idx, h] @ u[jh], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(st["dq_proj"][jh], sh["dq"][idx, h] @ u[jh], rtol=1e-10, atol=1e-12)
+        for d in range(8):
+            e = np.zeros((2, 8))
+            e[:, d] = 1.0
+            sb = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g, proj=e)
+            for jh, h in enumerate(range(2 * g, 2 * g + 2)):
+                np.testing.assert_allclose(sb["out_proj_sd"][jh], sd["out"][idx, h, d], rtol=1e-9, atol=1e-15)
+                np.testing.assert_allclose(sb["dq_proj_sd"][jh], sd["dq"][idx, h, d], rtol=1e-9, atol=1e-15)
