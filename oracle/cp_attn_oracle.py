@@ -761,6 +761,74 @@ def keys_dkdv_from_stats(stats: dict, q_bits, k_bits, v_bits, do_bits, cu, cup, 
     return dk, dv, np.sqrt(var_dk), np.sqrt(var_dv)
 
 
+def group_key_projections(stats: dict, q_bits, k_bits, v_bits, do_bits, cu, cup, scale: float, u_dk, u_dv,
+                          max_elems: int = 1 << 24) -> dict:
+    """Second pass over every key row at once, projected: for every valid
+    global key row j of the stats' KV head, the rank's contribution to dK_j
+    and dV_j (the same sums as keys_dkdv_from_stats) projected on the unit
+    vectors u_dk and u_dv,
+
+        dk_proj_j = <dK_j, u_dk>,   dv_proj_j = <dV_j, u_dv>,
+
+    and, for the comparison tolerance only, their standard deviations under
+    the rounding model of share_rounding_sd taken along u_dk / u_dv (with a
+    unit basis vector: that model's per-element deviations). Keys are taken
+    in blocks so that each block's score matrix stays below ``max_elems``.
+    Returns {"key_rows": global rows [n], "dk_proj", "dv_proj",
+    "dk_proj_sd", "dv_proj_sd": [n]}; key rows no query of the rank reaches
+    get 0.
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    cup = np.asarray(cup, dtype=np.int64)
+    g, group = stats["kv_head"], stats["group"]
+    u_dk = np.asarray(u_dk, dtype=np.float64)
+    u_dv = np.asarray(u_dv, dtype=np.float64)
+    c = BF16_UNIT_ROUNDOFF ** 2 / 3.0
+    keys, dkp, dvp, vdk, vdv = [], [], [], [], []
+    for b in range(cu.size - 1):
+        base = int(cup[b])
+        Lb = int(cu[b + 1] - cu[b])
+        if Lb == 0:
+            continue
+        sel = np.nonzero(stats["seq"] == b)[0]
+        kf = bf16_to_f64(k_bits[base:base + Lb, g])
+        vf = bf16_to_f64(v_bits[base:base + Lb, g])
+        acc = np.zeros((4, Lb))  # dk_proj, dv_proj, var_dk_proj, var_dv_proj
+        if sel.size:
+            pos = stats["pos"][sel]
+            heads = []
+            for jh, h in enumerate(range(g * group, (g + 1) * group)):
+                Q = bf16_to_f64(q_bits[stats["rows"][sel], h])
+                dO = bf16_to_f64(do_bits[stats["rows"][sel], h])
+                heads.append((Q, dO, Q @ u_dk, dO @ u_dv, stats["lse"][jh, sel], stats["dcoef"][jh, sel],
+                              c * stats["var_d_terms"][jh, sel]))
+            kb = max(1, min(Lb, max_elems // max(1, sel.size)))
+            for k0 in range(0, Lb, kb):
+                k1 = min(Lb, k0 + kb)
+                rq = pos >= k0  # query rows that reach some key of the block
+                if not rq.any():
+                    continue
+                mask = pos[rq][:, None] >= np.arange(k0, k1)[None, :]
+                K, V = kf[k0:k1], vf[k0:k1]
+                for Q, dO, Qu, dOu, lse, dco, vD in heads:
+                    S = scale * (Q[rq] @ K.T)
+                    P = np.where(mask, np.exp(S - lse[rq][:, None]), 0.0)
+                    dS = P * (dO[rq] @ V.T - dco[rq][:, None])
+                    acc[0, k0:k1] += scale * (Qu[rq] @ dS)
+                    acc[1, k0:k1] += dOu[rq] @ P
+                    acc[2, k0:k1] += c * scale ** 2 * ((Qu[rq] ** 2) @ (dS ** 2)) + \
+                        scale ** 2 * ((vD[rq] * Qu[rq] ** 2) @ (P ** 2))
+                    acc[3, k0:k1] += c * ((dOu[rq] ** 2) @ (P ** 2))
+        keys.append(base + np.arange(Lb))
+        dkp.append(acc[0])
+        dvp.append(acc[1])
+        vdk.append(acc[2])
+        vdv.append(acc[3])
+    cat = (lambda xs: np.concatenate(xs) if xs else np.zeros(0))
+    return {"key_rows": cat(keys).astype(np.int64), "dk_proj": cat(dkp), "dv_proj": cat(dvp),
+            "dk_proj_sd": np.sqrt(cat(vdk)), "dv_proj_sd": np.sqrt(cat(vdv))}
+
+
 def share_keys_dkdv_two_pass(q_bits, k_bits, v_bits, do_bits, cu, cup, cp: int, r: int, scale: float,
                              shard: int, key_local_rows, kv_head: int, stats: dict | None = None):
     """dK / dV rows of shard `shard`'s part of rank r's share for the selected

@@ -4,7 +4,9 @@ GQA share, CP = 4, rank 2, and the 64K hierarchical pack's p2p share, CP = 2,
 rank 0), for one KV head each, and the exact LSE of every query row of the
 rank for that KV head's query heads (a by-product of the first pass), with
 every such row's output and query gradient projected on a seeded unit
-vector per head and the rounding model's deviation of each projection.
+vector per head and the rounding model's deviation of each projection, and
+the rank's dK / dV of every valid key row (all source shards) projected the
+same way.
 
 Calls only the oracle (its two-pass key-row helper) and the seeded input
 generator; nothing comes from the HIP path. The inputs the values depend on
@@ -81,6 +83,18 @@ def main():
         arrays[pre + "proj_u"] = u
         for nm in ("out_proj", "dq_proj", "out_proj_sd", "dq_proj_sd"):
             arrays[pre + nm] = stats[nm].astype(np.float32)
+        # every valid key row's dK / dV (global order), projected
+        uk = np.random.default_rng(7100 + cfg).standard_normal((2, bt.d))
+        uk /= np.linalg.norm(uk, axis=1, keepdims=True)
+        t1 = time.time()
+        kp = O.group_key_projections(stats, bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, scale, uk[0], uk[1])
+        print(f"{bt.name}: projected dK / dV of {kp['key_rows'].size} key rows in {time.time() - t1:.1f} s", flush=True)
+        assert np.array_equal(kp["key_rows"], np.nonzero(O.valid_mask(bt.cu, bt.cup))[0])
+        arrays[pre + "key_u"] = uk
+        for nm in ("dk_proj", "dv_proj"):
+            arrays[pre + nm] = kp[nm].astype(np.float32)
+        for nm in ("dk_proj_sd", "dv_proj_sd"):
+            arrays[pre + nm] = kp[nm].astype(np.float16)
         for s in range(cp):
             rows = key_rows(t_local, bt.cu, bt.cup, cp, s)
             dk, dv, dks, dvs = O.share_keys_dkdv_two_pass(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale,

@@ -71,3 +71,30 @@ def test_fixture_lse_rows(cfg):
         np.testing.assert_allclose(a[:, pick], want, rtol=1e-5, atol=1e-7)
         sd = fx[pre + name + "_sd"]
         assert sd.shape == lse.shape and np.isfinite(sd).all() and (sd >= 0).all()
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_fixture_key_projections(cfg):
+    """Every valid key row's projected dK / dV: one value per key row in
+    global order, and on the last key rows (few queries reach them) the
+    oracle's one-pass key-row routine projected on the stored vectors."""
+    fx = np.load(OUT, allow_pickle=False)
+    bt, w = synth.make_workload(cfg)
+    pre = f"w{cfg}_"
+    cp, r, g = (int(x) for x in fx[pre + "meta"])
+    keys = np.nonzero(O.valid_mask(bt.cu, bt.cup))[0]
+    uk = fx[pre + "key_u"]
+    assert uk.shape == (2, bt.d) and np.allclose(np.linalg.norm(uk, axis=1), 1.0)
+    for nm in ("dk_proj", "dv_proj", "dk_proj_sd", "dv_proj_sd"):
+        a = fx[pre + nm]
+        assert a.shape == keys.shape and np.isfinite(a).all()
+    # the rank's own shard's last local key rows (local order = global
+    # positions the owner map sends there)
+    t_local = bt.total_rows // cp
+    late = np.array([t_local - 2, t_local - 1])
+    dk, dv = O.share_keys_dkdv(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, 1.0 / math.sqrt(bt.d), r, late, [g])
+    glob = O.shard_rows(bt.cu, bt.cup, cp, r)[late]
+    at = np.searchsorted(keys, glob)
+    assert np.array_equal(keys[at], glob)
+    np.testing.assert_allclose(fx[pre + "dk_proj"][at], dk[:, 0] @ uk[0], rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(fx[pre + "dv_proj"][at], dv[:, 0] @ uk[1], rtol=1e-5, atol=1e-7)

@@ -4,7 +4,8 @@ the 64K hierarchical-pack share), in the same launch configuration.
 The whole share is too large for the oracle, so: out / LSE / dQ are checked on
 sampled rows (each row one full softmax row of the oracle), and for every row
 of one KV head's query heads the LSE and the out and dQ rows projected on a
-fixed unit vector against stored oracle values; dK / dV element by
+fixed unit vector against stored oracle values, and that KV head's dK and dV
+rows projected the same way on every key row of every part; dK / dV element by
 element on key rows at the start, middle and end of every source shard's part
 (so every ring step's launch, the causal one included, and key rows that all
 of the rank's queries reach), against values the oracle's two-pass helper
@@ -172,6 +173,36 @@ def test_out_dq_every_row_projected_vs_oracle_fixture(full):
             assert bad.size == 0, (f"{name} head {heads[jh]}: {bad.size} rows over the bar, first local row "
                                    f"{int(rows[bad[0]])}: {gp[bad[0]]:.6g} vs {ref[jh, bad[0]]:.6g}")
         H.log(f"[full] {name} projected on every row ({rows.size} x {group}): worst / bar {worst:.3f}")
+
+
+def test_dkdv_every_key_row_projected_vs_oracle_fixture(full):
+    """The rank's dK and dV of every valid key row of one KV head, in every
+    source shard's part, projected on the stored unit vectors, against the
+    oracle's exact projections (bar as for out / dQ: the elements' own bf16
+    rounding, six of the rounding model's deviations of the projection, 1e-5
+    of the row's norm)."""
+    bt, w, r, scale, res = full
+    cfg = 4 if bt.hkv != bt.hq else 5
+    fx = np.load(FIXTURE, allow_pickle=False)
+    pre = f"w{cfg}_"
+    cp, rank, g = (int(x) for x in fx[pre + "meta"])
+    keys = np.nonzero(O.valid_mask(bt.cu, bt.cup))[0]
+    owner, local = O.owner_map(bt.cu, bt.cup, cp)
+    uk = fx[pre + "key_u"]
+    for name, j in (("dk", 0), ("dv", 1)):
+        got = np.zeros((keys.size, bt.d))
+        for s in range(cp):
+            m = owner[keys] == s
+            got[m] = H.bf16_bits_to_f64(res[name][s][local[keys[m]], g])
+        gp = got @ uk[j]
+        ref = fx[pre + name + "_proj"].astype(np.float64)
+        sd = fx[pre + name + "_proj_sd"].astype(np.float64)
+        tol = 2.0 ** -8 * (np.abs(got) @ np.abs(uk[j])) + 6.0 * sd + 1e-5 * np.linalg.norm(got, axis=1) + 1e-7
+        ratio = np.abs(gp - ref) / tol
+        bad = np.nonzero(ratio > 1.0)[0]
+        assert bad.size == 0, (f"{name}: {bad.size} key rows over the bar, first global row {int(keys[bad[0]])}: "
+                               f"{gp[bad[0]]:.6g} vs {ref[bad[0]]:.6g}")
+        H.log(f"[full] {name} projected on every key row ({keys.size}, {cp} parts): worst / bar {ratio.max():.3f}")
 
 
 def _tol(vals):

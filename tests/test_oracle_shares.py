@@ -256,3 +256,32 @@ def test_row_projections_match_full_share():
             for jh, h in enumerate(range(2 * g, 2 * g + 2)):
                 np.testing.assert_allclose(sb["out_proj_sd"][jh], sd["out"][idx, h, d], rtol=1e-9, atol=1e-15)
                 np.testing.assert_allclose(sb["dq_proj_sd"][jh], sd["dq"][idx, h, d], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("cp,hq,hkv,pad,seed", [(2, 4, 2, True, 51), (3, 6, 2, False, 52), (1, 2, 1, True, 53)])
+def test_key_projections_match_full_share(cp, hq, hkv, pad, seed):
+    """The blocked second pass's projected dK / dV of every key row equal the
+    full share's dK / dV (global order) projected on the same vectors, with
+    blocks small enough to split every sequence; along unit basis vectors its
+    deviations are the per-element rounding model's."""
+    bt = _random_batch(seed, cp, 3, hq, hkv, 8, pad)
+    scale = 0.35
+    rng = np.random.default_rng(seed)
+    valid = O.valid_mask(bt.cu, bt.cup)
+    for r in range(cp):
+        sh = O.share(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
+        sd = O.share_rounding_sd(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale)
+        for g in range(hkv):
+            st = O.group_row_stats(bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, cp, r, scale, g)
+            u, v = rng.standard_normal(8), rng.standard_normal(8)
+            kp = O.group_key_projections(st, bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, scale, u, v, max_elems=7)
+            rows = kp["key_rows"]
+            assert np.array_equal(rows, np.nonzero(valid)[0])
+            np.testing.assert_allclose(kp["dk_proj"], sh["dk_full"][rows, g] @ u, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(kp["dv_proj"], sh["dv_full"][rows, g] @ v, rtol=1e-10, atol=1e-12)
+            for d in (0, 5):
+                e = np.zeros(8)
+                e[d] = 1.0
+                kb = O.group_key_projections(st, bt.q, bt.k, bt.v, bt.do, bt.cu, bt.cup, scale, e, e, max_elems=7)
+                np.testing.assert_allclose(kb["dk_proj_sd"], sd["dk_full"][rows, g, d], rtol=1e-9, atol=1e-15)
+                np.testing.assert_allclose(kb["dv_proj_sd"], sd["dv_full"][rows, g, d], rtol=1e-9, atol=1e-15)
