@@ -158,10 +158,12 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
   KCopy kc;
   kc.init(ldb, w, lane);
   // a step's view for this block: its rows (slot-relative [rlo, rhi)), its
-  // keys, and how many 64-key tiles the block visits (0: the step does not
-  // reach the block's rows)
+  // keys, how many 64-key tiles the block visits (0: the step does not
+  // reach the block's rows), where its K and V rows start and the byte end
+  // of its key range (end32; -1 when a tile offset could pass 2^31, which
+  // then takes 64-bit arithmetic)
   struct View {
-    int rlo, rhi, kl, nt, causal;
+    int rlo, rhi, kl, nt, causal, end32;
     const uint16_t* kb;
     const uint16_t* vb;
   };
@@ -177,12 +179,20 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 8 / NWAVES) bwd_dq_kernel(BwdPa
     const long long kvs = tab(i, 2);
     v.kb = st.k[i] + kvs * p.ld_kv + kvh * D;
     v.vb = st.v[i] + kvs * p.ld_kv + kvh * D;
+    const long long end = (long long)v.kl * ldb;
+    v.end32 = end <= 0x7fffffffLL ? (int)end : -1;
     return v;
   };
   auto issue = [&](const View& v, int kt, auto buf) {
-    const long long off = (long long)kt * BN * ldb, end = (long long)v.kl * ldb;
-    kc.copy(rsrc_from(v.kb, off, end), ks_of(buf), w);
-    kc.copy(rsrc_from(v.vb, off, end), vs_of(buf), w);
+    if (v.end32 >= 0) {
+      const int off = kt * (BN * ldb);  // below end32, so below 2^31
+      kc.copy(rsrc_from32(v.kb, off, v.end32), ks_of(buf), w);
+      kc.copy(rsrc_from32(v.vb, off, v.end32), vs_of(buf), w);
+    } else {
+      const long long off = (long long)kt * BN * ldb, end = (long long)v.kl * ldb;
+      kc.copy(rsrc_from(v.kb, off, end), ks_of(buf), w);
+      kc.copy(rsrc_from(v.vb, off, end), vs_of(buf), w);
+    }
   };
   // the first step with work, then (step, tile) in order
   int i = 0;

@@ -206,9 +206,14 @@ __global__ void __launch_bounds__(BLOCK_THREADS, BN == 32 ? 3 : 8 / NWAVES) fwd_
   const int ldb = (int)(p.ld_kv * 2);
   // A position in the block's sequence of key tiles: entry j, key tile kt of
   // its nt, with the entry's query rows [rlo, rhi) (relative to qs), keys,
-  // first key row in its shard and mask kind.
+  // mask kind, and where its K and V rows start (kb, vb) with the byte end
+  // of its key range (end32; -1 when a tile offset could pass 2^31, which
+  // then takes 64-bit arithmetic). Everything but kt is set once per entry,
+  // so a tile's copy only adds its offset.
   struct Cur {
-    int j, kt, nt, rlo, rhi, kl, kvs, causal;
+    int j, kt, nt, rlo, rhi, kl, causal, end32;
+    const uint16_t* kb;
+    const uint16_t* vb;
   };
   auto at = [&](int j) {
     Cur u;
@@ -217,8 +222,12 @@ __global__ void __launch_bounds__(BLOCK_THREADS, BN == 32 ? 3 : 8 / NWAVES) fwd_
     u.rlo = FUSED ? tab(j, 0) - qs : 0;
     u.rhi = FUSED ? u.rlo + tab(j, 1) : ql;
     u.kl = tab(j, 3);
-    u.kvs = tab(j, 2);
     u.causal = st.kind[j] == 0;
+    const long long row0 = (long long)tab(j, 2) * p.ld_kv + kvh * D;
+    u.kb = st.k[j] + row0;
+    u.vb = st.v[j] + row0;
+    const long long end = (long long)u.kl * ldb;
+    u.end32 = end <= 0x7fffffffLL ? (int)end : -1;
     const int lo = max(q0, u.rlo), hi = min(q0 + nq, u.rhi);
     const int n_keys = hi <= lo ? 0 : (u.causal ? min(u.kl, q0 + nq) : u.kl);
     u.nt = (n_keys + BN - 1) / BN;
@@ -241,10 +250,15 @@ __global__ void __launch_bounds__(BLOCK_THREADS, BN == 32 ? 3 : 8 / NWAVES) fwd_
   kc.init(ldb, w, lane);
   vc.init(ldb, w, lane);
   auto issue = [&](const Cur& u, int buf) {
-    const long long off = (long long)u.kt * BN * ldb, end = (long long)u.kl * ldb;
-    const long long row0 = (long long)u.kvs * p.ld_kv + kvh * D;
-    kc.copy(rsrc_from(st.k[u.j] + row0, off, end), Ks[buf], w);
-    vc.copy(rsrc_from(st.v[u.j] + row0, off, end), Vs[buf], w);
+    if (u.end32 >= 0) {
+      const int off = u.kt * (BN * ldb);  // below end32, so below 2^31
+      kc.copy(rsrc_from32(u.kb, off, u.end32), Ks[buf], w);
+      vc.copy(rsrc_from32(u.vb, off, u.end32), Vs[buf], w);
+    } else {
+      const long long off = (long long)u.kt * BN * ldb, end = (long long)u.kl * ldb;
+      kc.copy(rsrc_from(u.kb, off, end), Ks[buf], w);
+      vc.copy(rsrc_from(u.vb, off, end), Vs[buf], w);
+    }
   };
 
   const float lazy_thr = 8.0f / c;  // 2^8 headroom, in raw score units

@@ -130,3 +130,51 @@ def test_work_lists_past_sort_cap():
     rnd = 2.0 ** -9 * np.sqrt((dk_all ** 2).sum(axis=0))
     assert (np.abs(dk_all.sum(axis=0)) / (6 * std + 8 * rnd + 1e-6)).max() <= 1.0
     meta.close()
+
+
+def test_kv_shard_past_2gib():
+    """One 262144-token sequence at CP = 1 with 32 KV heads of 128: each K / V
+    shard spans 2^31 bytes, so the forward and dQ kernels take their 64-bit
+    tile addressing (shorter key ranges use 32-bit offsets). Sampled out /
+    LSE / dQ rows and the last key rows' dK / dV against the oracle."""
+    import torch
+    T, cp, r, hq, hkv, d = 262144, 1, 0, 32, 32, 128
+    scale = 1.0 / math.sqrt(d)
+    cu = np.array([0, T], dtype=np.int32)
+    assert T * hkv * d * 2 >= 2 ** 31
+    H.log(f"[big kv] T={T} hq={hq} hkv={hkv}: K shard {T * hkv * d * 2 / 2**30:.2f} GiB")
+    meta = api.cp_attn_rank_metadata(H.dev_i32(cu), H.dev_i32(cu.copy()), cp, r, -1, T)
+    g = {nm: synth.device_normal_bf16((T, h, d), seed) for nm, h, seed in
+         (("q", hq, 71), ("k", hkv, 72), ("v", hkv, 73), ("do", hq, 74))}
+    loc = {"q": g["q"], "do": g["do"], "k": [g["k"]], "v": [g["v"]], "t_alloc": T, "t_local": T}
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 127, T // 2, T - 2, T - 1], rng.integers(T - 4096, T, 4)]))
+    heads = [0, 31]
+    keys = np.arange(T - 4, T)
+    # host copies of what the oracle reads: every key / value row of the
+    # checked heads' KV heads, the sampled query rows and the rows after the
+    # first checked key
+    need = np.unique(np.concatenate([rows, np.arange(keys[0], T)]))
+    qh = np.zeros((T, hq, d), dtype=np.uint16)
+    doh = np.zeros((T, hq, d), dtype=np.uint16)
+    idx = torch.from_numpy(need).to("cuda")
+    qh[need] = _bits(g["q"].index_select(0, idx))
+    doh[need] = _bits(g["do"].index_select(0, idx))
+    kh, vh = _bits(g["k"]), _bits(g["v"])
+    bt = synth.PackedBatch(name="big-kv", seed=71, cu=cu, cup=cu.copy(), hq=hq, hkv=hkv, d=d, q=qh, k=kh, v=vh, do=doh)
+    H.log("[big kv] GPU fwd + bwd")
+    out, lse = H.run_fwd(meta, loc, bt, scale)
+    dq, dks, dvs = H.run_bwd(meta, loc, bt, scale, out, lse)
+    torch.cuda.synchronize()
+    H.log(f"[big kv] oracle: {rows.size} rows x {len(heads)} heads")
+    o, l, dqr = O.share_rows(qh, kh, vh, doh, cu, cu, cp, r, scale, rows, heads, want_dq=True)
+    ridx = torch.from_numpy(rows).to("cuda")
+    H.compare_bf16("out", _bits(out.index_select(0, ridx)[:, heads]), o)
+    H.compare_lse("lse", lse[heads][:, ridx].cpu().numpy(), l)
+    H.compare_bf16("dq", _bits(dq.index_select(0, ridx)[:, heads]), dqr)
+    H.log(f"[big kv] oracle: dK / dV of {keys.size} key rows")
+    dk, dv = O.share_keys_dkdv(qh, kh, vh, doh, cu, cu, cp, r, scale, r, keys, [0, hkv - 1])
+    kidx = torch.from_numpy(keys).to("cuda")
+    H.compare_bf16("dk", _bits(dks[0].index_select(0, kidx)[:, [0, hkv - 1]]), dk)
+    H.compare_bf16("dv", _bits(dvs[0].index_select(0, kidx)[:, [0, hkv - 1]]), dv)
+    meta.close()
