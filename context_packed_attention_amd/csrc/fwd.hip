@@ -288,15 +288,17 @@ __global__ void __launch_bounds__(BLOCK_THREADS, BN == 32 ? 3 : 8 / NWAVES) fwd_
     if (masked) {
       // a real branch (kept out of if-conversion), taken on few tiles
       __asm__ volatile("" ::: "memory");
+      // element (mb, j) holds key k0 + 4 g + off, off = 32 mb + 8 (j / 4) +
+      // j % 4; it counts when the key is below lim (the range end, and at
+      // the causal step the row's own position + 1; nothing for rows outside
+      // the entry): one compare of off against a per-lane bound
       const bool row_in = !FUSED || (qrow >= u.rlo && qrow < u.rhi);
+      const int lim = !row_in ? -(1 << 20) : (u.causal ? min(u.kl, qrow + 1) : u.kl);
+      const int r = lim - 1 - (k0 + 4 * g);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + mb * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
-          const bool ok = row_in && key < u.kl && (!u.causal || key <= qrow);
-          s[mb][j] = ok ? s[mb][j] : NEG_INF_F;
-        }
+        for (int j = 0; j < 16; ++j) s[mb][j] = (r - (mb * 32 + (j >> 2) * 8 + (j & 3)) >= 0) ? s[mb][j] : NEG_INF_F;
     }
     float mx = NEG_INF_F;
 #pragma unroll
