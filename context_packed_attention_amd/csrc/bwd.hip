@@ -376,15 +376,22 @@ __global__ void __launch_bounds__(BLOCK_THREADS, (8 / NWAVES / DKDV_KB) > 0 ? 8 
 
   if (n_iter > 0) {
     // K rows of this lane's keys in registers, the block's V rows in LDS
+    // (every lane loads from a valid row, row 0 of the range for keys past
+    // it, and zeroes those afterwards: the loads issue back to back, with no
+    // branch between them)
     bf16x8_t kf[KB][NKK];
+    const uint16_t* const kshard = sts.k[si];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = k0 + wr0 + kb * 32 + l32;
       const bool ok = key < kl;
-      const long long off = (long long)(kvs + (ok ? key : 0)) * p.ld_kv + kvh * D + g * 8;
+      const uint4* const src =
+          reinterpret_cast<const uint4*>(kshard + (long long)(kvs + (ok ? key : 0)) * p.ld_kv + kvh * D + g * 8);
+      uint4 u[NKK];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kf[kb][kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(sts.k[si] + off + kk * 16) : make_uint4(0, 0, 0, 0));
+      for (int kk = 0; kk < NKK; ++kk) u[kk] = src[2 * kk];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kf[kb][kk] = as_bf16x8(ok ? u[kk] : make_uint4(0, 0, 0, 0));
     }
     {
       const int ldkv = (int)(p.ld_kv * 2);
