@@ -313,6 +313,21 @@ __global__ void meta_tiles_kernel(int32_t* __restrict__ tabp, MetaLayout L, int 
       int rows = min(FWD_BM, q_len - t * FWD_BM);
       int keys_n = kind == 0 ? min(kv_len, (t + 1) * FWD_BM) : kv_len;
       work = (long long)rows * keys_n;
+      if (i == 0) {
+        // step 0's items are also the blocks of the single-launch forward,
+        // where each block runs the key tiles of every step its rows take
+        // part in: the sum of those steps' keys, for the whole block
+        const int q0 = t * FWD_BM, q1 = q0 + rows;
+        long long keys_all = 0;
+        for (int j = 0; j < cp; ++j) {
+          const int32_t* sj = tabp + L.steps + (int64_t)j * 4 * B;
+          const int rlo = sj[b] - st[b], rhi = rlo + sj[B + b];
+          if (max(q0, rlo) >= min(q1, rhi)) continue;
+          const int kl = sj[3 * B + b];
+          keys_all += sw[SW_KIND + j] == 0 ? min(kl, q1) : kl;
+        }
+        work = (long long)FWD_BM * keys_all;
+      }
     } else {
       int nk = clampi(kv_len - t * DKDV_BN, 0, DKDV_BN);
       int nq = kind == 0 ? max(0, q_len - t * DKDV_BN) : q_len;

@@ -19,6 +19,10 @@ SMALL = [
     ("ragged-cp3-d128-gqa", [600, 1, 250, 0], [600, 12, 252, 6], 3, 8, 2, 128),
     ("long-cp4-d128", [1800, 500], [1808, 504], 4, 4, 4, 128),
     ("tiny-cp4-d64-pad", [5, 9, 1], [8, 16, 8], 4, 2, 2, 64),
+    # one long sequence among many short ones: the single-launch forward's
+    # work list, ordered by each item's keys over all ring steps, starts with
+    # the long sequence's last query tiles
+    ("mixed-cp2-d128", [2048] + [64] * 40, [2048] + [64] * 40, 2, 2, 2, 128),
 ]
 
 
