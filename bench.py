@@ -2,9 +2,10 @@
 """Benchmark: one CP rank's share of packed-THD causal ring attention, fwd+bwd.
 
 One step = the whole hot path over one batch: the per-rank metadata build,
-the forward (one flash kernel per ring step + LSE merges) and the backward
-(D preprocess, per-step dK/dV and dQ kernels, dQ finalize, tail zeroing when a
-tail exists). Beside it, the forward + backward captured once as a HIP graph is
+the forward (one flash kernel per ring step, each folding its partial into the
+accumulator through the LSE merge, or for short shares one launch over every
+step) and the backward (D preprocess, one dK/dV launch over every step, one
+dQ launch, tail zeroing when a tail exists). Beside it, the forward + backward captured once as a HIP graph is
 timed against the same calls made eagerly (the "graph" object). Inputs are seeded synthetic bf16 tensors already resident in
 HBM. The reported value is algorithmic TFLOP/s: 14 * D * Hq * causal pairs of
 the share per step (4 forward + 10 backward), divided by the measured time.
@@ -32,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # figure with the SHA-256 of the kernel sources it was taken on, and the
 # figure is dropped once those sources change
 TRAFFIC_SOURCES = ("context_packed_attention_amd/csrc/bwd.hip", "context_packed_attention_amd/csrc/fwd.hip",
-                   "context_packed_attention_amd/csrc/kern_common.h", "context_packed_attention_amd/csrc/internal.h")
+                   "context_packed_attention_amd/csrc/kern_common.h", "context_packed_attention_amd/csrc/internal.h",
+                   "context_packed_attention_amd/csrc/meta.hip")
 
 
 def kernel_sources_sha256():
